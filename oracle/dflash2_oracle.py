@@ -1,0 +1,447 @@
+"""CPU oracle of the DFlash2 block draft -> select -> verify step.
+
+TEST INFRASTRUCTURE.  This module is the plain, slow statement of what the
+step computes.  Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import it; the GPU library never does, and nothing here is
+shared with it (decoders, norms, RoPE, attention, ranking and the dynamic
+program are all written out again below).
+
+Sources (page title, section):
+  [AM]  NeMo AutoModel, "Train a DFlash Drafter for Speculative Decoding":
+        §What is DFlash?, §Variants (table, row "DFlash 2"), §Objective,
+        §Data (note on mask_token_id), §Key Config Fields (table).
+  [VL]  NeMo SpeechLM, "DFlash speculative decoding with vLLM":
+        intro, §DFlash2 inference, §Validation.
+  [LC]  llama-cpp-python wiki, "DFlash2 Speculative Decoding":
+        §Prerequisites, §Configuration Notes.
+  [NIM] NVIDIA NIM for Alpamayo, "DFlash2 Speculative Decoding":
+        §Observe Acceptance (metrics fields table).
+
+Precision: the network (context append, block forward, logits) runs in
+float64 on the exact values of the stored inputs (bf16 and fp32 decode
+exactly, fp8 decodes to code * scale).  Appended cache rows are rounded to
+the cache dtype because the caller sees them.  Ranking (top-k), the selector
+dynamic program and verification run in exact IEEE float32 with a fixed
+operation order, so their integer outputs can be compared bit for bit.
+
+Readings of points the pages leave open are labelled Q1..Q30 (the numbering
+of the design notes); each function names the ones it takes.
+
+Parity pins: every function except `draft_block`/`step` as a whole is pinned
+by tests against brute force, closed forms or library special cases.  The
+composition of the whole draft forward has no worked example on the pages:
+parity unpinned for the composed network beyond its pinned parts and the
+special-case invariants in tests/test_oracle_draft.py.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Decoding stored bytes into exact values (independent of the encoders).
+# ----------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 is the top half of an IEEE binary32: widen and reinterpret."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u32.view(np.float32).astype(np.float64)
+
+
+def fp8_e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP e4m3fn: sign, 4-bit exponent (bias 7), 3-bit mantissa; exponent 0
+    is subnormal (m/8 * 2^-6); code 0x7F/0xFF is NaN; no infinities."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+def decode_rows(t, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
+    """Exact float64 values of rows [r0, r1) of a stored tensor."""
+    r1 = t.data.shape[0] if r1 is None else r1
+    x = t.data[r0:r1]
+    if t.dtype == "fp32":
+        return x.astype(np.float64)
+    if t.dtype == "bf16":
+        return bf16_bits_to_f64(x)
+    if t.dtype == "fp8":
+        return fp8_e4m3fn_to_f64(x) * t.scale[r0:r1].astype(np.float64)[:, None]
+    raise ValueError(t.dtype)
+
+
+def decode(t) -> np.ndarray:
+    return decode_rows(t)
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to what a cache of `dtype` stores (fp32 or bf16,
+    nearest-even), returned as float64 values."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)  # IEEE RNE
+    if dtype == "fp32":
+        return x32.astype(np.float64)
+    u = x32.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Building blocks.
+# ----------------------------------------------------------------------------
+
+
+def linear(x: np.ndarray, w, rows: Optional[tuple] = None, chunk_elems: int = 1 << 26) -> np.ndarray:
+    """y = x . W^T for a stored weight W[out, in] (row-major [out, in], as
+    every linear of the draft is stored).  `rows` selects a contiguous block
+    of output rows.  The weight is decoded a block of output rows at a time to
+    bound memory; every output is a full-length dot product."""
+    r0, r1 = (0, w.data.shape[0]) if rows is None else rows
+    K = w.data.shape[1]
+    step = max(1, chunk_elems // K)
+    y = np.empty(x.shape[:-1] + (r1 - r0,), dtype=np.float64)
+    x2 = x.reshape(-1, K)
+    y2 = y.reshape(-1, r1 - r0)
+    for a in range(r0, r1, step):
+        b = min(r1, a + step)
+        y2[:, a - r0:b - r0] = x2 @ decode_rows(w, a, b).T
+    return y
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * g.
+    [AM §What is DFlash?: the draft trains its own norms; Q8: RMSNorm]."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half rotary embedding (Q14).  x [..., n, d] with one position
+    per leading row n: for i < d/2 the pair (x_i, x_{i+d/2}) is rotated by the
+    angle pos * theta^(-2i/d)."""
+    d = x.shape[-1]
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * theta ** (-2.0 * i / d)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    shape = (len(pos),) + (1,) * (x.ndim - 2) + (half,)
+    c, s = c.reshape(shape), s.reshape(shape)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def block_conv(x: np.ndarray, taps: np.ndarray) -> np.ndarray:
+    """In-block depthwise convolution in correction form (Q10-Q13):
+    y[t] = x[t] + sum_{j<K} taps[j] * x[t-j], with x[t-j] = 0 before slot 0.
+    [AM §Variants, DFlash 2: a two-tap in-block convolution around every
+    sublayer; it never reaches outside the block]."""
+    bs = x.shape[0]
+    y = x.copy()
+    for j in range(taps.shape[0]):
+        y[j:] += taps[j] * x[:bs - j]
+    return y
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Unmasked (non-causal) softmax attention with grouped KV heads.
+    q [T, nq, d], k/v [S, nkv, d] -> [T, nq, d].  q-head i reads kv head
+    i // (nq / nkv).  [AM §What is DFlash?: the block is denoised in one
+    non-causal pass]."""
+    T, nq, d = q.shape
+    nkv = k.shape[1]
+    grp = nq // nkv
+    out = np.empty_like(q)
+    for i in range(nq):
+        g = i // grp
+        s = q[:, i, :] @ k[:, g, :].T / math.sqrt(d)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out[:, i, :] = p @ v[:, g, :]
+    return out
+
+
+def logit_transform(x: np.ndarray, multiplier: float, softcap: float) -> np.ndarray:
+    """The target's logit transform (Q16): m*x, then cap*tanh(x/cap) when a
+    cap is set.  [AM §Key Config Fields: output_multiplier /
+    final_logit_softcapping, identity unless set]."""
+    y = multiplier * x
+    if softcap > 0:
+        y = softcap * np.tanh(y / softcap)
+    return y
+
+
+# ----------------------------------------------------------------------------
+# O1: context append.
+# ----------------------------------------------------------------------------
+
+
+def new_cache(w, batch: int, k_init: Optional[np.ndarray] = None, v_init=None):
+    """float64 K and V caches [nL, B, nkv, Lmax, d] (logical row order),
+    optionally initialised from stored rows (fp32 values or bf16 bits)."""
+    shape = (w.num_layers, batch, w.num_kv_heads, w.max_context, w.head_dim)
+
+    def conv(a):
+        if a is None:
+            return np.zeros(shape)
+        return a.astype(np.float64) if a.dtype == np.float32 else bf16_bits_to_f64(a)
+    return conv(k_init), conv(v_init)
+
+
+def append_context(w, W, k_cache, v_cache, taps, new_offsets, ctx_lens) -> np.ndarray:
+    """Project the target hidden-state taps of the newly verified positions
+    and write every layer's context keys/values.
+
+    [AM §What is DFlash?: the draft is conditioned on hidden states taken
+    from the frozen target at target_layer_ids and owns a feature
+    projection; LC §Tips: the draft keeps its own context.]
+    Readings: Q4 taps concatenated on the feature axis in target_layer_ids
+    order; Q5 one bias-free projection then RMSNorm; Q6 each layer projects
+    the same feature with its own K/V rows of W_qkv, K stored after RoPE;
+    Q2 new rows sit at positions L - n_new .. L - 1.
+    Returns the normalised features f [sum n_new, H]."""
+    nq, nkv, d = w.num_q_heads, w.num_kv_heads, w.head_dim
+    tv = decode(taps)
+    n_rows = tv.shape[0]
+    if n_rows == 0:
+        return np.zeros((0, w.hidden))
+    u = tv.reshape(n_rows, w.num_taps * w.tap_width)
+    f = rmsnorm(linear(u, W.proj), decode(W.proj_norm), w.rms_eps)
+    pos = np.empty(n_rows, dtype=np.int64)
+    seq = np.empty(n_rows, dtype=np.int64)
+    for b in range(len(ctx_lens)):
+        o0, o1 = int(new_offsets[b]), int(new_offsets[b + 1])
+        pos[o0:o1] = int(ctx_lens[b]) - (o1 - o0) + np.arange(o1 - o0)
+        seq[o0:o1] = b
+    for l, layer in enumerate(W.layers):
+        kv = linear(f, layer.wqkv, rows=(nq * d, (nq + 2 * nkv) * d))
+        kk = rope(kv[:, :nkv * d].reshape(n_rows, nkv, d), pos, w.rope_theta)
+        vv = kv[:, nkv * d:].reshape(n_rows, nkv, d)
+        kk = round_to_storage(kk, w.act_dtype)
+        vv = round_to_storage(vv, w.act_dtype)
+        for r in range(n_rows):
+            k_cache[l, seq[r], :, pos[r], :] = kk[r]
+            v_cache[l, seq[r], :, pos[r], :] = vv[r]
+    return f
+
+
+# ----------------------------------------------------------------------------
+# O2-O4: block forward and logits.
+# ----------------------------------------------------------------------------
+
+
+def draft_block(w, W, k_cache, v_cache, anchors, ctx_lens) -> Dict[str, np.ndarray]:
+    """One non-causal forward of the draft over a block per sequence.
+
+    [AM §What is DFlash?: slot 0 is the real anchor token, the other slots
+    hold MASK, the whole block is denoised in one non-causal pass using the
+    target's frozen embed_tokens and lm_head; AM §Data: the mask id is a
+    reserved token; AM §Variants: DFlash 2 adds a two-tap in-block
+    convolution around every sublayer; AM §Key Config Fields:
+    input_embedding_scale, output_multiplier / final_logit_softcapping,
+    draft_sliding_window.]
+    Readings: Q1 slot t predicts the token at slot t; Q2 slot t sits at
+    position L + t; Q3 context = projected taps only; Q13 conv before each
+    sublayer's pre-norm on the residual stream, none before the final norm;
+    Q14 RoPE; Q15 SwiGLU; Q18 logits for slots 1..bs-1 only.
+
+    Returns zeta [B, bs-1, V] (float64 logits before the transform) and
+    h_final [B, bs, H] (residual stream after the last layer)."""
+    B, bs, H = len(anchors), w.block_size, w.hidden
+    nq, nkv, d = w.num_q_heads, w.num_kv_heads, w.head_dim
+    tokens = np.full((B, bs), w.mask_token_id, dtype=np.int64)
+    tokens[:, 0] = anchors
+    E = W.embed
+    h = np.stack([w.input_embedding_scale * decode_rows(E, int(t), int(t) + 1)[0]
+                  for t in tokens.reshape(-1)]).reshape(B, bs, H)
+    pos = np.asarray(ctx_lens, dtype=np.int64)[:, None] + np.arange(bs)[None, :]
+    for l, layer in enumerate(W.layers):
+        ca, cf = decode(layer.conv_attn), decode(layer.conv_ffn)
+        h = np.stack([block_conv(h[b], ca) for b in range(B)])
+        n = rmsnorm(h, decode(layer.attn_norm), w.rms_eps)
+        qkv = linear(n, layer.wqkv)                       # [B, bs, (nq+2nkv)d]
+        o = np.empty((B, bs, nq * d))
+        for b in range(B):
+            L = int(ctx_lens[b])
+            q = rope(qkv[b, :, :nq * d].reshape(bs, nq, d), pos[b], w.rope_theta)
+            kb = rope(qkv[b, :, nq * d:(nq + nkv) * d].reshape(bs, nkv, d), pos[b], w.rope_theta)
+            vb = qkv[b, :, (nq + nkv) * d:].reshape(bs, nkv, d)
+            lo = max(0, L - w.sliding_window) if w.sliding_window > 0 else 0
+            kc = k_cache[l, b, :, lo:L, :].transpose(1, 0, 2)  # [S, nkv, d]
+            vc = v_cache[l, b, :, lo:L, :].transpose(1, 0, 2)
+            o[b] = attention(q, np.concatenate([kc, kb]), np.concatenate([vc, vb])).reshape(bs, nq * d)
+        h = h + linear(o, layer.wo)
+        h = np.stack([block_conv(h[b], cf) for b in range(B)])
+        n = rmsnorm(h, decode(layer.ffn_norm), w.rms_eps)
+        gu = linear(n, layer.w_gate_up)
+        act = silu(gu[..., :w.ffn]) * gu[..., w.ffn:]
+        h = h + linear(act, layer.w_down)
+    nf = rmsnorm(h[:, 1:, :], decode(W.final_norm), w.rms_eps)
+    zeta = linear(nf, W.lm_head)
+    return {"zeta": zeta, "h_final": h}
+
+
+# ----------------------------------------------------------------------------
+# O5: top-k candidates per block position.
+# ----------------------------------------------------------------------------
+
+
+def canonical_f32(x: np.ndarray) -> np.ndarray:
+    """float32 keys with -0.0 turned into +0.0 (Q23)."""
+    return np.asarray(x, dtype=np.float32) + np.float32(0.0)
+
+
+def topk(keys32: np.ndarray, k: int):
+    """The k largest entries of each row under (value desc, id asc), in that
+    order, found by k rounds of "take the first maximum, then strike it out"
+    (Q23).  keys32 [R, V] float32.  [AM §Variants: the selector walks each
+    position's top-k candidates; LC §Configuration Notes: selector_top_k is
+    fixed by the head]."""
+    x = canonical_f32(keys32).astype(np.float64)
+    R = x.shape[0]
+    ids = np.empty((R, k), dtype=np.int32)
+    vals = np.empty((R, k), dtype=np.float32)
+    taken = np.zeros(x.shape, dtype=bool)
+    rows = np.arange(R)
+    for j in range(k):
+        masked = np.where(taken, -np.inf, x)
+        a = np.argmax(masked, axis=1)        # first occurrence: smallest id among equals
+        ids[:, j] = a
+        vals[:, j] = x[rows, a]
+        taken[rows, a] = True
+    return ids, vals
+
+
+# ----------------------------------------------------------------------------
+# O6: pairwise low-rank path selector.
+# ----------------------------------------------------------------------------
+
+
+def pair_scores(tl: np.ndarray, tr: np.ndarray, a_ids: np.ndarray, b_ids: np.ndarray) -> np.ndarray:
+    """pi(a, b) = sum_m Tl[a, m] * Tr[b, m] in float32, multiply then add,
+    m ascending from +0 (Q21, Q25).  Returns [len(a), len(b)] float32."""
+    A = tl[np.asarray(a_ids)].astype(np.float32)      # [na, r]
+    Bm = tr[np.asarray(b_ids)].astype(np.float32)     # [nb, r]
+    acc = np.zeros((A.shape[0], Bm.shape[0]), dtype=np.float32)
+    for m in range(A.shape[1]):
+        prod = (A[:, m][:, None] * Bm[:, m][None, :]).astype(np.float32)
+        acc = (acc + prod).astype(np.float32)
+    return acc
+
+
+def select_path(anchors, cand_ids, cand_vals, tl, tr) -> Dict[str, np.ndarray]:
+    """Max-sum (Viterbi) path through the per-position candidate lattice.
+
+    [AM §Variants: a pairwise path selector picks one coherent path through
+    every position's top-k; AM §Objective: each position's candidates are
+    scored against the ground-truth predecessor; LC §Complete Runnable Code: the selector
+    lattice replaces vocabulary sampling.]
+    Readings: Q19 first-order chain starting at the anchor; Q20 unary term =
+    the candidate's logit; Q21 pair term = rank-r bilinear form through the
+    factor tables; Q26 the smallest predecessor index wins a tie, and the
+    smallest final index.  Arithmetic in float32:
+        S_1[j] = pi(c0, c_1j) + z_1j
+        S_t[j] = max_i (S_{t-1}[i] + pi(c_{t-1,i}, c_tj)) + z_tj
+    cand_ids/cand_vals [B, P, k]; returns path [B, P] (candidate ranks),
+    drafts [B, P] (token ids), score [B] float32 and pair [B, P, k, k]
+    (row i of slab 0 repeats pi(c0, .))."""
+    cand_ids = np.asarray(cand_ids)
+    cand_vals = np.asarray(cand_vals, dtype=np.float32)
+    B, P, k = cand_ids.shape
+    path = np.empty((B, P), dtype=np.int32)
+    drafts = np.empty((B, P), dtype=np.int32)
+    score = np.empty(B, dtype=np.float32)
+    pair = np.empty((B, P, k, k), dtype=np.float32)
+    for b in range(B):
+        p0 = pair_scores(tl, tr, [int(anchors[b])], cand_ids[b, 0])[0]
+        pair[b, 0] = p0[None, :]
+        S = (p0 + cand_vals[b, 0]).astype(np.float32)
+        back = np.zeros((P, k), dtype=np.int64)
+        for t in range(1, P):
+            pt = pair_scores(tl, tr, cand_ids[b, t - 1], cand_ids[b, t])
+            pair[b, t] = pt
+            tot = (S[:, None] + pt).astype(np.float32)       # [i, j]
+            bi = np.argmax(tot, axis=0)                      # first max over i
+            back[t] = bi
+            S = (tot[bi, np.arange(k)] + cand_vals[b, t]).astype(np.float32)
+        j = int(np.argmax(S))
+        score[b] = S[j]
+        for t in range(P - 1, -1, -1):
+            path[b, t] = j
+            drafts[b, t] = cand_ids[b, t, j]
+            j = int(back[t, j])
+    return {"path": path, "drafts": drafts, "score": score, "pair": pair}
+
+
+# ----------------------------------------------------------------------------
+# O7: greedy verification.
+# ----------------------------------------------------------------------------
+
+
+def verify_accept(drafts, target_logits) -> Dict[str, np.ndarray]:
+    """Longest accepted prefix under greedy verification.
+
+    [VL intro and §Validation: the target checks the drafts and accepted
+    output equals the target's greedy output; LC §Prerequisites: the target
+    scores [last id, drafts...] in one batch; NIM §Observe Acceptance: the
+    verified token counts towards each step's output.]
+    Reading Q27: row i of the target logits is the target's prediction after
+    block slot i; draft d_{i+1} (drafts[:, i]) is accepted while it equals
+    that row's argmax; the bonus token is the argmax of the first row that
+    disagrees (row bs-1 when every draft is accepted).  Argmax ties go to the
+    smallest id after -0.0 -> +0.0."""
+    drafts = np.asarray(drafts)
+    z = canonical_f32(target_logits)
+    B, bs, V = z.shape
+    g = np.argmax(z, axis=2).astype(np.int32)
+    accepted = np.zeros(B, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n = 0
+        while n < bs - 1 and g[b, n] == drafts[b, n]:
+            n += 1
+        accepted[b] = n
+        bonus[b] = g[b, n]
+    return {"accepted": accepted, "bonus": bonus, "argmax": g}
+
+
+# ----------------------------------------------------------------------------
+# The whole step.
+# ----------------------------------------------------------------------------
+
+
+def step(w, W, inp, target_logits_fn=None) -> Dict[str, np.ndarray]:
+    """O1..O7 for the sequences in `inp`.  `target_logits_fn(drafts)`
+    supplies the verifier's logits for the chosen drafts (None skips
+    verification)."""
+    B = len(inp.anchors)
+    k_cache, v_cache = new_cache(w, B, inp.k_ctx, inp.v_ctx)
+    f = append_context(w, W, k_cache, v_cache, inp.taps, inp.new_offsets, inp.ctx_lens)
+    fwd = draft_block(w, W, k_cache, v_cache, inp.anchors, inp.ctx_lens)
+    zeta = fwd["zeta"]
+    keys32 = zeta.astype(np.float32).reshape(-1, w.vocab)
+    ids, _ = topk(keys32, w.top_k)
+    z = logit_transform(zeta, w.output_multiplier, w.final_logit_softcapping).astype(np.float32)
+    z = z.reshape(-1, w.vocab)
+    vals = np.take_along_axis(z, ids.astype(np.int64), axis=1)
+    P = w.block_size - 1
+    ids = ids.reshape(B, P, w.top_k)
+    vals = vals.reshape(B, P, w.top_k)
+    sel = select_path(inp.anchors, ids, vals, W.sel_tl.data, W.sel_tr.data)
+    out = {"f": f, "k_cache": k_cache, "v_cache": v_cache, "zeta": zeta,
+           "h_final": fwd["h_final"], "topk_ids": ids, "topk_vals": vals, **sel}
+    if target_logits_fn is not None:
+        tl = target_logits_fn(sel["drafts"])
+        out.update(verify_accept(sel["drafts"], tl))
+        out["target_logits"] = tl
+    return out
