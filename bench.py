@@ -1,0 +1,188 @@
+"""Throughput of the DFlash2 draft -> select -> verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = dflash2_draft_block (context append, block forward, lm_head +
+top-k) + dflash2_select_path + dflash2_verify_accept over one batch of
+seeded synthetic inputs already resident in HBM.  Default workload: the
+27B-class single-sequence draft (batch 1, block 8, hidden 5120, 5 layers,
+vocab 151936, bf16).  Prints one JSON line: drafted blocks/s (value) and
+draft tokens/s, the roofline of the dominant kernel measured with HIP
+events over a traced repeat of the timed steps, and the CPU oracle's
+throughput on the same workload (one block) as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "fp32": 157.3}  # fp8 weights run as bf16 MFMA (W8A16)
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense27b_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the step shards by sequence with no exchange, so "
+              f"--gpus {args.gpus} is not supported (run one process per GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from block_speculative_decoding_dflash2_amd import DFlash2, to_device, verify_accept, verify_workspace
+    from block_speculative_decoding_dflash2_amd.runner import KernelTrace
+    from block_speculative_decoding_dflash2_amd.metrics import speculative_metrics
+
+    w = synth.get(args.workload)
+    t0 = time.time()
+    W = synth.make_weights(w)
+    inp = synth.make_step_inputs(w)
+    log(f"generated {w.name} inputs in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    model = DFlash2(w.abi_config(), W, device=dev)
+    kc, vc = model.new_caches()
+    model.load_context(kc, vc, inp.k_ctx, inp.v_ctx)
+    anchors = torch.from_numpy(inp.anchors).to(dev)
+    offsets = torch.from_numpy(inp.new_offsets).to(dev)
+    ctx_lens = torch.from_numpy(inp.ctx_lens).to(dev)
+    taps = to_device(inp.taps.data.reshape(inp.taps.data.shape[0], -1), dev)
+    max_new = int(inp.new_offsets[-1])
+    B, bs, V, k = w.batch, w.block_size, w.vocab, w.top_k
+    ws = model.workspace(B, max_new)
+    topk_ids = torch.empty((B, bs - 1, k), dtype=torch.int32, device=dev)
+    topk_vals = torch.empty((B, bs - 1, k), dtype=torch.float32, device=dev)
+    path = torch.empty((B, bs - 1), dtype=torch.int32, device=dev)
+    drafts = torch.empty((B, bs - 1), dtype=torch.int32, device=dev)
+    accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    vws = verify_workspace(B, bs, V, dev)
+
+    # verifier logits planted around the drafts of a first (untimed) step
+    model.draft_block(anchors, taps, offsets, ctx_lens, max_new, kc, vc, workspace=ws,
+                      topk_ids=topk_ids, topk_vals=topk_vals)
+    model.select_path(anchors, topk_ids, topk_vals, path_idx=path, draft_tokens=drafts, want_score=False)
+    torch.cuda.synchronize()
+    target = torch.from_numpy(synth.make_target_logits(w, drafts.cpu().numpy())).to(dev)
+
+    def step():
+        model.draft_block(anchors, taps, offsets, ctx_lens, max_new, kc, vc, workspace=ws,
+                          topk_ids=topk_ids, topk_vals=topk_vals)
+        model.select_path(anchors, topk_ids, topk_vals, path_idx=path, draft_tokens=drafts,
+                          want_score=False)
+        verify_accept(drafts, target, workspace=vws, accepted=accepted, bonus=bonus)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    s_step = elapsed / args.steps
+    log(f"{args.steps} steps in {elapsed * 1e3:.2f} ms -> {s_step * 1e6:.1f} us/step")
+
+    roofline = None
+    per_kind = {}
+    if not args.no_trace:
+        tr = KernelTrace(capacity=args.steps * 128 + 64)
+        with tr:
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
+        recs = tr.records()
+        tr.close()
+        for kind, by, fl, ms in recs:
+            d = per_kind.setdefault(kind, {"launches": 0, "ms": 0.0, "bytes": 0, "flops": 0})
+            d["launches"] += 1
+            d["ms"] += ms
+            d["bytes"] += by
+            d["flops"] += fl
+        traced_total = sum(d["ms"] for d in per_kind.values())
+        dom = max(per_kind, key=lambda kk: per_kind[kk]["ms"])
+        d = per_kind[dom]
+        secs = d["ms"] / 1e3
+        ai = d["flops"] / max(d["bytes"], 1)
+        mfma_peak = MFMA_PEAK_TFLOPS[w.weight_dtype]
+        ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if ai < ridge:
+            achieved = d["bytes"] / secs / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+        else:
+            achieved = d["flops"] / secs / 1e12
+            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                        "frac": round(achieved / mfma_peak, 4), "traffic": None}
+        roofline.update({"kernel": dom, "launches_per_step": d["launches"] // args.steps,
+                         "avg_launch_us": round(d["ms"] * 1e3 / d["launches"], 2),
+                         "bytes_per_launch": d["bytes"] // d["launches"],
+                         "share_of_kernel_time": round(d["ms"] / traced_total, 3)})
+        for kind, dd in sorted(per_kind.items(), key=lambda kv: -kv[1]["ms"]):
+            log(f"  {kind:15s} {dd['launches'] // args.steps:3d}/step {dd['ms'] * 1e3 / args.steps:9.1f} us/step "
+                f"{dd['bytes'] / max(dd['ms'], 1e-9) / 1e6:8.1f} GB/s")
+        log(f"  kernel time {traced_total * 1e3 / args.steps:.1f} us/step (wall {s_step * 1e6:.1f})")
+
+    acc = accepted.cpu().numpy()
+    spec = speculative_metrics(acc.tolist(), bs - 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        from threadpoolctl import threadpool_info
+        nthreads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t1 = time.time()
+        O.step(w, W, inp)
+        dt = time.time() - t1
+        cpu = {"value": round(B / dt, 6), "unit": "blocks/s", "cores": int(nthreads), "kind": "oracle",
+               "sample": f"one full step of {w.name} ({B} block(s)); float64 NumPy oracle, {dt:.1f}s"}
+        log(f"oracle step {dt:.1f}s with {nthreads} BLAS threads")
+
+    out = {
+        "metric": "drafted blocks/s per MI355X",
+        "value": round(B / s_step, 2),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.weight_dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps and context, planted-argmax verifier logits)",
+        "config": {"workload": w.name, "batch": B, "block_size": bs, "hidden": w.hidden,
+                   "draft_layers": w.num_layers, "heads": f"{w.num_q_heads}/{w.num_kv_heads}x{w.head_dim}",
+                   "ffn": w.ffn, "taps": f"{w.num_taps}x{w.tap_width}", "context": list(w.ctx),
+                   "vocab": V, "top_k": k, "selector_rank": w.rank, "parallelism": "none (1 GPU)"},
+        "draft_tokens_per_s": round(B * (bs - 1) / s_step, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "acceptance": {kk: spec[kk] for kk in ("draft_acceptance_rate", "mean_acceptance_length")},
+        "kernels_us_per_step": {kk: round(dd["ms"] * 1e3 / args.steps, 2) for kk, dd in per_kind.items()},
+    }
+    print(json.dumps(out), flush=True)
+    model.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,544 @@
+// Host side of the C ABI: argument validation, work planning (split-K
+// factors, attention chunking, workspace carve-up) and the launch sequence
+// of one draft step.  No device memory is allocated and no call
+// synchronises; everything is enqueued on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "dflash2.h"
+#include "kernels.h"
+
+using namespace dfl;
+
+struct dflash2_handle {
+  dflash2_config cfg;
+  dflash2_weights w;
+  std::vector<dflash2_layer_weights> layers;
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+dflash2_status fail(dflash2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+dflash2_status ok() {
+  g_error.clear();
+  return DFLASH2_OK;
+}
+
+// Per-thread kernel trace (see dflash2_trace_attach).
+struct Trace {
+  dflash2_trace_entry* entries = nullptr;
+  int32_t capacity = 0, count = 0;
+};
+thread_local Trace g_trace;
+
+template <typename F>
+void traced(hipStream_t s, int kind, int64_t bytes, int64_t flops, F&& launch) {
+  Trace& t = g_trace;
+  dflash2_trace_entry* e = (t.entries && t.count < t.capacity) ? &t.entries[t.count++] : nullptr;
+  if (e) {
+    e->kind = kind;
+    e->bytes = bytes;
+    e->flops = flops;
+    hipEventRecord(e->start, s);
+  }
+  launch();
+  if (e) hipEventRecord(e->stop, s);
+}
+
+// Plans are a pure function of the shapes (not of the device), so results
+// and workspace sizes do not depend on which GPU runs them.
+constexpr int kTargetBlocks = 512;  // 2 blocks of 4 waves per CU on 256 CUs
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int act_bytes(const dflash2_config& c) { return c.weight_dtype == DFLASH2_FP32 ? 4 : 2; }
+int weight_bytes(const dflash2_config& c) {
+  return c.weight_dtype == DFLASH2_FP32 ? 4 : (c.weight_dtype == DFLASH2_BF16 ? 2 : 1);
+}
+
+struct Split {
+  int splits = 1, k_split = 0;
+};
+
+Split plan_split(int dtype, int M, int N, int K) {
+  Split s;
+  const int mtile = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+  const int64_t blocks = cdiv(N, gemm_rows_per_block(dtype, M)) * cdiv(M, mtile);
+  int S = 1;
+  if (M <= 64) {
+    S = int(cdiv(kTargetBlocks, blocks));
+    S = std::min(S, std::max(1, K / 256));
+    S = std::min(S, 64);
+    S = std::max(S, 1);
+  }
+  s.k_split = int(cdiv(cdiv(K, S), 32) * 32);
+  s.splits = int(cdiv(K, s.k_split));
+  return s;
+}
+
+struct AttnPlan {
+  int chunk = 128, nchunks = 1, qgroups = 1, qs = 1;
+};
+
+// Chunks of whole LDS sub-chunks; enough sub-chunks per block that the grid
+// is about kTargetBlocks blocks (fewer, larger chunks mean fewer partials).
+AttnPlan plan_attn(const dflash2_config& c, int B) {
+  AttnPlan a;
+  const int grp = c.num_q_heads / c.num_kv_heads;
+  a.qs = c.block_size * grp;
+  a.qgroups = int(cdiv(a.qs, 64));
+  const int kt = attn_sub_chunk(c.weight_dtype == DFLASH2_FP32, c.head_dim);
+  const int64_t subs = cdiv(c.max_context, kt);
+  const int64_t heads = int64_t(B) * c.num_kv_heads * a.qgroups;
+  const int64_t per_block = std::max<int64_t>(1, cdiv(heads * subs, kTargetBlocks));
+  a.chunk = int(per_block * kt);
+  a.nchunks = int(cdiv(c.max_context, a.chunk));
+  return a;
+}
+
+struct Plan {
+  int B, M, Mh, Mn;
+  Split proj, kv, qkv, o, gu, down;
+  AttnPlan attn;
+  int groups;
+  size_t off_h0, off_h1, off_n, off_sumsq, off_q, off_o, off_a, off_parts, off_attn_o, off_attn_ml,
+      off_cand;
+  size_t total;
+};
+
+Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
+  Plan p;
+  p.B = B;
+  p.M = B * c.block_size;
+  p.Mh = B * (c.block_size - 1);
+  p.Mn = int(Mn);
+  const int H = c.hidden, qd = c.num_q_heads * c.head_dim, kvd = 2 * c.num_kv_heads * c.head_dim;
+  const int qkvd = qd + kvd, F = c.ffn, dt = c.weight_dtype;
+  p.proj = plan_split(dt, std::max(p.Mn, 1), H, c.num_taps * c.tap_width);
+  p.kv = plan_split(dt, std::max(p.Mn, 1), kvd, H);
+  p.qkv = plan_split(dt, p.M, qkvd, H);
+  p.o = plan_split(dt, p.M, H, qd);
+  p.gu = plan_split(dt, p.M, 2 * F, H);
+  p.down = plan_split(dt, p.M, H, F);
+  p.attn = plan_attn(c, B);
+  p.groups = int(cdiv(c.vocab, 256));
+  const size_t ab = act_bytes(c);
+  size_t parts = 0;
+  auto upd = [&](size_t v) { parts = std::max(parts, v); };
+  if (p.Mn > 0) {
+    upd(size_t(p.proj.splits) * p.Mn * H);
+    upd(size_t(c.num_layers) * p.kv.splits * p.Mn * kvd);
+  }
+  upd(size_t(p.qkv.splits) * p.M * qkvd);
+  upd(size_t(p.o.splits) * p.M * H);
+  upd(size_t(p.gu.splits) * p.M * 2 * F);
+  upd(size_t(p.down.splits) * p.M * H);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  p.off_h0 = take(size_t(p.M) * H * 4);
+  p.off_h1 = take(size_t(p.M) * H * 4);
+  p.off_n = take(size_t(std::max(p.M, p.Mn)) * H * ab);
+  p.off_sumsq = take(size_t(std::max(p.M, p.Mn)) * norm_col_blocks(H) * 4);
+  p.off_q = take(size_t(p.M) * qd * ab);
+  p.off_o = take(size_t(p.M) * qd * ab);
+  p.off_a = take(size_t(p.M) * F * ab);
+  p.off_parts = take(parts * 4);
+  const size_t attn_rows = size_t(B) * c.num_kv_heads * p.attn.nchunks * p.attn.qs;
+  p.off_attn_o = take(attn_rows * c.head_dim * 4);
+  p.off_attn_ml = take(attn_rows * 2 * 4);
+  p.off_cand = take(size_t(p.Mh) * p.groups * c.selector_top_k * 8);
+  p.total = off;
+  return p;
+}
+
+dflash2_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DFLASH2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DFLASH2_OK;
+}
+
+const void* byte_offset(const void* p, int64_t bytes) {
+  return static_cast<const char*>(p) + bytes;
+}
+
+size_t select_lds(int k, int r, int P) {
+  return size_t(2 * k * select_row_stride(r) + k * k + k + P * k) * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash2_last_error(void) { return g_error.c_str(); }
+
+dflash2_status dflash2_trace_attach(dflash2_trace_entry* entries, int32_t capacity) {
+  if (capacity < 0 || (capacity > 0 && !entries))
+    return fail(DFLASH2_ERR_INVALID_ARG, "trace_attach: bad entries/capacity");
+  g_trace.entries = entries;
+  g_trace.capacity = capacity;
+  g_trace.count = 0;
+  return ok();
+}
+
+int32_t dflash2_trace_detach(void) {
+  const int32_t n = g_trace.count;
+  g_trace = Trace();
+  return n;
+}
+
+dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weights* weights,
+                              dflash2_handle** out) {
+  if (!config || !weights || !out) return fail(DFLASH2_ERR_INVALID_ARG, "create: null argument");
+  *out = nullptr;
+  const dflash2_config& c = *config;
+  if (c.hidden <= 0 || c.num_layers <= 0 || c.num_q_heads <= 0 || c.num_kv_heads <= 0 ||
+      c.head_dim <= 0 || c.ffn <= 0 || c.vocab <= 0 || c.num_taps <= 0 || c.tap_width <= 0 ||
+      c.max_batch <= 0 || c.max_context <= 0 || c.sliding_window < 0)
+    return fail(DFLASH2_ERR_INVALID_ARG, "create: sizes must be positive");
+  if (c.weight_dtype < DFLASH2_FP32 || c.weight_dtype > DFLASH2_FP8_E4M3)
+    return fail(DFLASH2_ERR_INVALID_ARG, "create: unknown weight_dtype %d", c.weight_dtype);
+  if (c.block_size < 2) return fail(DFLASH2_ERR_SHAPE, "create: block_size %d < 2", c.block_size);
+  if (c.num_q_heads % c.num_kv_heads)
+    return fail(DFLASH2_ERR_SHAPE, "create: num_q_heads %d not a multiple of num_kv_heads %d",
+                c.num_q_heads, c.num_kv_heads);
+  if (c.conv_kernel_size < 1 || c.conv_kernel_size > c.block_size)
+    return fail(DFLASH2_ERR_SHAPE, "create: conv_kernel_size %d outside 1..block_size",
+                c.conv_kernel_size);
+  if (c.selector_top_k < 1 || c.selector_top_k > 64 || c.selector_top_k > c.vocab)
+    return fail(DFLASH2_ERR_SHAPE, "create: selector_top_k %d outside 1..min(64, vocab)",
+                c.selector_top_k);
+  if (c.selector_rank < 1 || c.selector_rank > 256)
+    return fail(DFLASH2_ERR_SHAPE, "create: selector_rank %d outside 1..256", c.selector_rank);
+  if (c.mask_token_id < 0 || c.mask_token_id >= c.vocab)
+    return fail(DFLASH2_ERR_SHAPE, "create: mask_token_id %d outside [0, vocab)", c.mask_token_id);
+  if (c.max_context < c.block_size)
+    return fail(DFLASH2_ERR_SHAPE, "create: max_context %d < block_size", c.max_context);
+  if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f) || !(c.final_logit_softcapping >= 0.f))
+    return fail(DFLASH2_ERR_INVALID_ARG, "create: bad rms_eps / rope_theta / softcap");
+  if (!attn_supported(c.head_dim))
+    return fail(DFLASH2_ERR_UNSUPPORTED, "create: head_dim %d not in {16, 32, 64, 128, 256}",
+                c.head_dim);
+  const int qd = c.num_q_heads * c.head_dim;
+  if (c.hidden % 32 || c.ffn % 32 || qd % 32 || (c.num_taps * c.tap_width) % 32)
+    return fail(DFLASH2_ERR_UNSUPPORTED,
+                "create: hidden, ffn, nq*head_dim and num_taps*tap_width must be multiples of 32");
+  if (c.hidden > 16384) return fail(DFLASH2_ERR_UNSUPPORTED, "create: hidden > 16384");
+  if (c.max_context % 8)
+    return fail(DFLASH2_ERR_UNSUPPORTED, "create: max_context must be a multiple of 8");
+  if (select_lds(c.selector_top_k, c.selector_rank, c.block_size - 1) > 64 * 1024)
+    return fail(DFLASH2_ERR_UNSUPPORTED, "create: selector_top_k * selector_rank too large");
+  const dflash2_weights& w = *weights;
+  if (!w.embed || !w.lm_head || !w.proj || !w.proj_norm || !w.final_norm || !w.sel_tl ||
+      !w.sel_tr || !w.layers)
+    return fail(DFLASH2_ERR_INVALID_ARG, "create: null weight pointer");
+  const bool fp8 = c.weight_dtype == DFLASH2_FP8_E4M3;
+  if (fp8 && (!w.lm_head_scale || !w.proj_scale))
+    return fail(DFLASH2_ERR_INVALID_ARG, "create: fp8 weights need scales");
+  for (int l = 0; l < c.num_layers; ++l) {
+    const dflash2_layer_weights& L = w.layers[l];
+    if (!L.conv_attn || !L.attn_norm || !L.wqkv || !L.wo || !L.conv_ffn || !L.ffn_norm ||
+        !L.w_gate_up || !L.w_down)
+      return fail(DFLASH2_ERR_INVALID_ARG, "create: null weight pointer in layer %d", l);
+    if (fp8 && (!L.wqkv_scale || !L.wo_scale || !L.w_gate_up_scale || !L.w_down_scale))
+      return fail(DFLASH2_ERR_INVALID_ARG, "create: fp8 weights need scales (layer %d)", l);
+  }
+  dflash2_handle* h = new dflash2_handle;
+  h->cfg = c;
+  h->w = w;
+  h->layers.assign(w.layers, w.layers + c.num_layers);
+  h->w.layers = h->layers.data();
+  *out = h;
+  return ok();
+}
+
+void dflash2_destroy(dflash2_handle* handle) { delete handle; }
+
+dflash2_status dflash2_workspace_size(const dflash2_handle* handle, int32_t batch,
+                                      int64_t max_new_rows, size_t* bytes) {
+  if (!handle || !bytes) return fail(DFLASH2_ERR_INVALID_ARG, "workspace_size: null argument");
+  if (batch < 1 || batch > handle->cfg.max_batch)
+    return fail(DFLASH2_ERR_SHAPE, "workspace_size: batch %d outside 1..max_batch", batch);
+  if (max_new_rows < 0 || max_new_rows > int64_t(1) << 30)
+    return fail(DFLASH2_ERR_SHAPE, "workspace_size: bad max_new_rows");
+  *bytes = make_plan(handle->cfg, batch, max_new_rows).total;
+  return ok();
+}
+
+dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                   const int32_t* anchor_ids, const void* new_taps,
+                                   const int32_t* new_offsets, const int32_t* ctx_lens,
+                                   int64_t max_new_rows, void* k_cache, void* v_cache,
+                                   int32_t* topk_ids, float* topk_vals, float* debug_logits,
+                                   float* debug_hidden, void* workspace, size_t workspace_bytes) {
+  if (!handle) return fail(DFLASH2_ERR_INVALID_ARG, "draft_block: null handle");
+  const dflash2_config& c = handle->cfg;
+  if (batch < 1 || batch > c.max_batch)
+    return fail(DFLASH2_ERR_SHAPE, "draft_block: batch %d outside 1..max_batch %d", batch, c.max_batch);
+  if (max_new_rows < 0 || max_new_rows > int64_t(1) << 30)
+    return fail(DFLASH2_ERR_SHAPE, "draft_block: bad max_new_rows");
+  if (!anchor_ids || !new_offsets || !ctx_lens || !k_cache || !v_cache || !topk_ids || !topk_vals ||
+      (max_new_rows > 0 && !new_taps))
+    return fail(DFLASH2_ERR_INVALID_ARG, "draft_block: null pointer argument");
+  const Plan P = make_plan(c, batch, max_new_rows);
+  if (!workspace || workspace_bytes < P.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return fail(DFLASH2_ERR_WORKSPACE, "draft_block: workspace needs %zu bytes, 256-aligned", P.total);
+
+  const bool f32 = c.weight_dtype == DFLASH2_FP32;
+  const int dt = c.weight_dtype;
+  const int H = c.hidden, nq = c.num_q_heads, nkv = c.num_kv_heads, d = c.head_dim, F = c.ffn;
+  const int qd = nq * d, kvd = 2 * nkv * d, qkvd = qd + kvd, bs = c.block_size;
+  const int wb = weight_bytes(c);
+  char* ws = static_cast<char*>(workspace);
+  float* h0 = reinterpret_cast<float*>(ws + P.off_h0);
+  float* h1 = reinterpret_cast<float*>(ws + P.off_h1);
+  void* nbuf = ws + P.off_n;
+  float* sumsq = reinterpret_cast<float*>(ws + P.off_sumsq);
+  // RMSNorm factor of the rows last written by norm(): applied by the next GEMM
+  const RowScale normed{sumsq, norm_col_blocks(H), 1.0f / float(H), c.rms_eps};
+  const RowScale plain{nullptr, 0, 0.f, 0.f};
+  void* qbuf = ws + P.off_q;
+  void* obuf = ws + P.off_o;
+  void* abuf = ws + P.off_a;
+  float* parts = reinterpret_cast<float*>(ws + P.off_parts);
+  const int64_t cache_layer = int64_t(c.max_batch) * nkv * c.max_context * d;
+  const int ab = act_bytes(c);
+  char* kc = static_cast<char*>(k_cache);
+  char* vc = static_cast<char*>(v_cache);
+  dflash2_status st;
+
+  auto gemm = [&](const void* X, int64_t ldx, const void* W, const float* scale, int M,
+                  const int32_t* M_dev, int N, int K, const Split& sp, float* out, const RowScale& rs) {
+    GemmArgs a{};
+    a.rs = rs;
+    a.X = X; a.ldx = ldx; a.W = W; a.ldw = K; a.scale = scale;
+    a.P = out; a.ldp = N; a.split_stride = int64_t(M) * N;
+    a.M = M; a.N = N; a.K = K; a.M_dev = M_dev;
+    a.splits = sp.splits; a.k_split = sp.k_split;
+    const int64_t bytes = int64_t(N) * K * wb + (scale ? int64_t(N) * 4 : 0) + int64_t(M) * K * ab +
+                          int64_t(M) * N * 4;
+    traced(stream, DFLASH2_K_GEMM, bytes, 2 * int64_t(M) * N * K, [&] { launch_gemm(dt, a, stream); });
+  };
+  auto norm = [&](int rows, const int32_t* rows_dev, int nbs, const void* embed, const float* base,
+                  const float* prt, const Split* sp, int64_t pstride, const void* conv,
+                  const void* gain, float* h_out, void* n_out, int t_first) {
+    NormArgs a{};
+    a.H = H; a.rows = rows; a.rows_dev = rows_dev; a.bs = nbs;
+    a.embed = embed; a.anchors = anchor_ids; a.mask_id = c.mask_token_id; a.vocab = c.vocab;
+    a.emb_scale = c.input_embedding_scale;
+    a.base = base; a.parts = prt; a.splits = sp ? sp->splits : 0; a.split_stride = pstride; a.ldp = H;
+    a.conv = conv; a.conv_k = c.conv_kernel_size; a.gain = gain;
+    a.h_out = h_out; a.n_out = n_out; a.sumsq = sumsq; a.t_first = t_first;
+    const int64_t in_rows = int64_t(rows) * H * ((embed ? ab : 0) + (base ? 4 : 0) + 4 * a.splits);
+    const int64_t out_rows = int64_t(rows) * H * ((h_out ? 4 : 0) + ab);
+    traced(stream, DFLASH2_K_NORM, in_rows + out_rows, 0, [&] { launch_norm(f32, a, stream); });
+  };
+
+  // ---- 1. context append -------------------------------------------------
+  if (P.Mn > 0) {
+    const int Kp = c.num_taps * c.tap_width;
+    const int32_t* rows_dev = new_offsets + batch;
+    gemm(new_taps, Kp, handle->w.proj, handle->w.proj_scale, P.Mn, rows_dev, H, Kp, P.proj, parts, plain);
+    norm(P.Mn, rows_dev, 1, nullptr, nullptr, parts, &P.proj, int64_t(P.Mn) * H, nullptr,
+         handle->w.proj_norm, nullptr, nbuf, 0);
+    const int64_t lstride = int64_t(P.kv.splits) * P.Mn * kvd;
+    for (int l = 0; l < c.num_layers; ++l) {
+      const dflash2_layer_weights& L = handle->layers[l];
+      const void* W = byte_offset(L.wqkv, int64_t(qd) * H * wb);
+      const float* sc = L.wqkv_scale ? L.wqkv_scale + qd : nullptr;
+      gemm(nbuf, H, W, dt == DFLASH2_FP8_E4M3 ? sc : nullptr, P.Mn, rows_dev, kvd, H, P.kv,
+           parts + l * lstride, normed);
+    }
+    KvAppendArgs ka{};
+    ka.parts = parts; ka.splits = P.kv.splits; ka.split_stride = int64_t(P.Mn) * kvd; ka.ldp = kvd;
+    ka.layer_stride = lstride; ka.offsets = new_offsets; ka.ctx_lens = ctx_lens;
+    ka.B = batch; ka.Mn = P.Mn; ka.nkv = nkv; ka.d = d; ka.Lmax = c.max_context; ka.nL = c.num_layers;
+    ka.cache_layer_stride = cache_layer; ka.theta = c.rope_theta;
+    ka.k_cache = k_cache; ka.v_cache = v_cache;
+    traced(stream, DFLASH2_K_KV_APPEND, int64_t(P.Mn) * c.num_layers * kvd * (4 * P.kv.splits + ab), 0,
+           [&] { launch_kv_append(f32, ka, stream); });
+    if ((st = check_launch("draft_block/append")) != DFLASH2_OK) return st;
+  }
+
+  // ---- 2. block forward --------------------------------------------------
+  const dflash2_layer_weights& L0 = handle->layers[0];
+  norm(P.M, nullptr, bs, handle->w.embed, nullptr, nullptr, nullptr, 0, L0.conv_attn, L0.attn_norm,
+       h0, nbuf, 0);
+  for (int l = 0; l < c.num_layers; ++l) {
+    const dflash2_layer_weights& L = handle->layers[l];
+    const bool fp8 = dt == DFLASH2_FP8_E4M3;
+    void* kl = kc + l * cache_layer * ab;
+    void* vl = vc + l * cache_layer * ab;
+    gemm(nbuf, H, L.wqkv, fp8 ? L.wqkv_scale : nullptr, P.M, nullptr, qkvd, H, P.qkv, parts, normed);
+    QkvEpiArgs qa{};
+    qa.parts = parts; qa.splits = P.qkv.splits; qa.split_stride = int64_t(P.M) * qkvd; qa.ldp = qkvd;
+    qa.ctx_lens = ctx_lens; qa.M = P.M; qa.bs = bs; qa.nq = nq; qa.nkv = nkv; qa.d = d;
+    qa.Lmax = c.max_context; qa.theta = c.rope_theta; qa.q_out = qbuf; qa.k_layer = kl; qa.v_layer = vl;
+    traced(stream, DFLASH2_K_QKV_EPILOGUE, int64_t(P.M) * qkvd * (4 * P.qkv.splits + ab), 0,
+           [&] { launch_qkv_epilogue(f32, qa, stream); });
+
+    AttnArgs aa{};
+    aa.q = qbuf; aa.k_layer = kl; aa.v_layer = vl; aa.ctx_lens = ctx_lens;
+    aa.B = batch; aa.bs = bs; aa.nq = nq; aa.nkv = nkv; aa.d = d; aa.Lmax = c.max_context;
+    aa.window = c.sliding_window; aa.chunk_keys = P.attn.chunk; aa.nchunks = P.attn.nchunks;
+    aa.qgroups = P.attn.qgroups;
+    aa.part_o = reinterpret_cast<float*>(ws + P.off_attn_o);
+    aa.part_ml = reinterpret_cast<float*>(ws + P.off_attn_ml);
+    aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(d)));
+    // keys/values of every sequence at the host-side bound max_context
+    const int64_t kv_bytes = int64_t(batch) * nkv * c.max_context * d * 2 * ab;
+    traced(stream, DFLASH2_K_ATTENTION, kv_bytes + int64_t(P.M) * qd * ab,
+           4 * int64_t(P.M) * qd * c.max_context, [&] { launch_attention(f32, aa, stream); });
+    AttnCombineArgs ca{};
+    ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.ctx_lens = ctx_lens;
+    ca.B = batch; ca.bs = bs; ca.nq = nq; ca.nkv = nkv; ca.d = d; ca.Lmax = c.max_context;
+    ca.window = c.sliding_window; ca.chunk_keys = P.attn.chunk; ca.nchunks = P.attn.nchunks;
+    ca.o = obuf;
+    traced(stream, DFLASH2_K_ATTN_COMBINE, int64_t(P.M) * qd * ab, 0,
+           [&] { launch_attn_combine(f32, ca, stream); });
+
+    gemm(obuf, qd, L.wo, fp8 ? L.wo_scale : nullptr, P.M, nullptr, H, qd, P.o, parts, plain);
+    norm(P.M, nullptr, bs, nullptr, h0, parts, &P.o, int64_t(P.M) * H, L.conv_ffn, L.ffn_norm, h1,
+         nbuf, 0);
+    gemm(nbuf, H, L.w_gate_up, fp8 ? L.w_gate_up_scale : nullptr, P.M, nullptr, 2 * F, H, P.gu, parts,
+         normed);
+    SwigluArgs sa{};
+    sa.parts = parts; sa.splits = P.gu.splits; sa.split_stride = int64_t(P.M) * 2 * F; sa.ldp = 2 * F;
+    sa.M = P.M; sa.F = F; sa.out = abuf;
+    traced(stream, DFLASH2_K_SWIGLU, int64_t(P.M) * F * (8 * P.gu.splits + ab), 0,
+           [&] { launch_swiglu(f32, sa, stream); });
+    gemm(abuf, F, L.w_down, fp8 ? L.w_down_scale : nullptr, P.M, nullptr, H, F, P.down, parts, plain);
+    if (l + 1 < c.num_layers) {
+      const dflash2_layer_weights& Ln = handle->layers[l + 1];
+      norm(P.M, nullptr, bs, nullptr, h1, parts, &P.down, int64_t(P.M) * H, Ln.conv_attn,
+           Ln.attn_norm, h0, nbuf, 0);
+    } else {
+      norm(P.M, nullptr, bs, nullptr, h1, parts, &P.down, int64_t(P.M) * H, nullptr,
+           handle->w.final_norm, debug_hidden, nbuf, 1);
+    }
+    if ((st = check_launch("draft_block/layer")) != DFLASH2_OK) return st;
+  }
+
+  // ---- 3. lm_head + top-k --------------------------------------------------
+  LmHeadArgs la{};
+  la.X = nbuf; la.ldx = H; la.W = handle->w.lm_head; la.ldw = H;
+  la.scale = dt == DFLASH2_FP8_E4M3 ? handle->w.lm_head_scale : nullptr;
+  la.M = P.Mh; la.N = c.vocab; la.K = H; la.M_dev = nullptr; la.groups = P.groups;
+  la.k = c.selector_top_k; la.cand = reinterpret_cast<uint64_t*>(ws + P.off_cand);
+  la.debug_logits = debug_logits;
+  la.rs = normed;
+  {
+    const int64_t bytes = int64_t(c.vocab) * H * wb + (la.scale ? int64_t(c.vocab) * 4 : 0) +
+                          int64_t(P.Mh) * H * ab + int64_t(P.Mh) * c.selector_top_k * 8 +
+                          (debug_logits ? int64_t(P.Mh) * c.vocab * 4 : 0);
+    traced(stream, DFLASH2_K_LMHEAD_TOPK, bytes, 2 * int64_t(P.Mh) * c.vocab * H,
+           [&] { launch_lmhead_topk(dt, la, stream); });
+  }
+  TopkMergeArgs ma{};
+  ma.cand = la.cand; ma.count = P.groups * c.selector_top_k; ma.M = P.Mh; ma.k = c.selector_top_k;
+  ma.M_dev = nullptr; ma.ids = topk_ids; ma.vals = topk_vals;
+  ma.multiplier = c.output_multiplier; ma.softcap = c.final_logit_softcapping;
+  traced(stream, DFLASH2_K_TOPK_MERGE, int64_t(P.Mh) * ma.count * 8 + int64_t(P.Mh) * ma.k * 8, 0,
+         [&] { launch_topk_merge(ma, stream); });
+  if ((st = check_launch("draft_block/lm_head")) != DFLASH2_OK) return st;
+  return ok();
+}
+
+dflash2_status dflash2_select_path(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                   const int32_t* anchor_ids, const int32_t* topk_ids,
+                                   const float* topk_vals, int32_t* path_idx,
+                                   int32_t* draft_tokens, float* path_score, float* debug_pair) {
+  if (!handle) return fail(DFLASH2_ERR_INVALID_ARG, "select_path: null handle");
+  const dflash2_config& c = handle->cfg;
+  if (batch < 1 || batch > c.max_batch)
+    return fail(DFLASH2_ERR_SHAPE, "select_path: batch %d outside 1..max_batch %d", batch, c.max_batch);
+  if (!anchor_ids || !topk_ids || !topk_vals || !path_idx || !draft_tokens)
+    return fail(DFLASH2_ERR_INVALID_ARG, "select_path: null pointer argument");
+  SelectArgs a{};
+  a.anchors = anchor_ids; a.ids = topk_ids; a.vals = topk_vals;
+  a.tl = handle->w.sel_tl; a.tr = handle->w.sel_tr;
+  a.B = batch; a.P = c.block_size - 1; a.k = c.selector_top_k; a.r = c.selector_rank; a.V = c.vocab;
+  a.path = path_idx; a.drafts = draft_tokens; a.score = path_score; a.debug_pair = debug_pair;
+  {
+    const int64_t pairs = int64_t(batch) * (int64_t(a.P - 1) * a.k * a.k + a.k);
+    const int64_t bytes = int64_t(batch) * a.P * a.k * 8 + int64_t(batch) * (a.P * a.k + 1) * 2 * a.r * 4 +
+                          int64_t(batch) * a.P * 8;
+    traced(stream, DFLASH2_K_SELECT, bytes, 2 * pairs * a.r,
+           [&] { launch_select(a, select_lds(a.k, a.r, a.P), stream); });
+  }
+  dflash2_status st = check_launch("select_path");
+  return st == DFLASH2_OK ? ok() : st;
+}
+
+namespace {
+struct VerifyPlan {
+  int nchunks, chunk;
+  size_t bytes;
+};
+VerifyPlan plan_verify(int B, int bs, int V) {
+  VerifyPlan v;
+  const int64_t rows = int64_t(B) * bs;
+  int64_t n = std::max<int64_t>(1, cdiv(2048, rows));
+  n = std::min<int64_t>(n, std::max<int64_t>(1, cdiv(V, 4096)));
+  v.chunk = int(cdiv(cdiv(V, n), 256) * 256);
+  v.nchunks = int(cdiv(V, v.chunk));
+  v.bytes = align_up(size_t(rows) * v.nchunks * 8);
+  return v;
+}
+}  // namespace
+
+dflash2_status dflash2_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
+                                             size_t* bytes) {
+  if (!bytes) return fail(DFLASH2_ERR_INVALID_ARG, "verify_workspace_size: null argument");
+  if (batch < 1 || block_size < 2 || vocab < 1)
+    return fail(DFLASH2_ERR_SHAPE, "verify_workspace_size: bad sizes");
+  *bytes = plan_verify(batch, block_size, vocab).bytes;
+  return ok();
+}
+
+dflash2_status dflash2_verify_accept(hipStream_t stream, int32_t batch, int32_t block_size,
+                                     int32_t vocab, const int32_t* draft_tokens,
+                                     const float* target_logits, int32_t* accepted,
+                                     int32_t* bonus, int32_t* target_argmax, void* workspace,
+                                     size_t workspace_bytes) {
+  if (batch < 1 || block_size < 2 || vocab < 1)
+    return fail(DFLASH2_ERR_SHAPE, "verify_accept: bad sizes (batch %d, block_size %d, vocab %d)",
+                batch, block_size, vocab);
+  if (!draft_tokens || !target_logits || !accepted || !bonus)
+    return fail(DFLASH2_ERR_INVALID_ARG, "verify_accept: null pointer argument");
+  const VerifyPlan vp = plan_verify(batch, block_size, vocab);
+  if (!workspace || workspace_bytes < vp.bytes || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return fail(DFLASH2_ERR_WORKSPACE, "verify_accept: workspace needs %zu bytes, 256-aligned", vp.bytes);
+  VerifyArgs a{};
+  a.drafts = draft_tokens; a.logits = target_logits;
+  a.B = batch; a.bs = block_size; a.V = vocab; a.nchunks = vp.nchunks; a.chunk = vp.chunk;
+  a.part = static_cast<uint64_t*>(workspace);
+  a.accepted = accepted; a.bonus = bonus; a.argmax = target_argmax;
+  traced(stream, DFLASH2_K_VERIFY_PARTIAL, int64_t(batch) * block_size * vocab * 4, 0,
+         [&] { launch_verify_partial(a, stream); });
+  traced(stream, DFLASH2_K_VERIFY_FINAL, int64_t(batch) * (block_size - 1) * 4 + int64_t(batch) * 8, 0,
+         [&] { launch_verify_final(a, stream); });
+  dflash2_status st = check_launch("verify_accept");
+  return st == DFLASH2_OK ? ok() : st;
+}
+
+}  // extern "C"

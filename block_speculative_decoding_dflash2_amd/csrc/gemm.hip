@@ -1,0 +1,386 @@
+// Weight-streaming GEMMs y = x * W^T on the gfx950 matrix cores.
+//
+// Every linear of the draft (feature projection, QKV, O, gate/up, down) and
+// the lm_head multiplies a few activation rows (B * block_size) by a large
+// weight.  With few rows the work is bound by reading the weight once from
+// HBM.  Each wave owns 16*RT weight rows and a K range and walks it in
+// groups of 256 bytes per row.  A group is loaded with non-temporal 16-byte
+// loads in which each quarter-wave reads 256 contiguous bytes of one row (4
+// rows per instruction); on this chip that pattern streams ~37% faster than
+// loading straight into the MFMA operand layout (16 rows x 64 bytes per
+// instruction).  The group then goes through a wave-private LDS tile (rows
+// padded to 272 bytes, conflict-free) and is read back as MFMA operands.
+// Loads run NSG groups ahead of the math in a ring of register stages; the
+// activation fragments of a group (small, L2-resident) ride in the same ring.
+//
+// Splitting K over the grid's z dimension gives enough waves to cover all 256
+// CUs when a weight has few rows; each split writes float32 partial sums that
+// the consumer kernel reduces in a fixed order (deterministic results).
+//
+// fp8 weights (e4m3fn + one float32 scale per output row) are widened to bf16
+// when read from LDS (exact) and the scale is applied to the partial sums.
+#include "common.h"
+#include "kernels.h"
+
+namespace dfl {
+
+// One MFMA A-operand fragment (8 k-values of one row) read from the LDS copy
+// of a weight group: bf16 16 bytes, fp8 8 bytes (widened), fp32 32 bytes.
+template <typename TW> struct LdsFrag;
+template <> struct LdsFrag<bf16_t> {
+  typedef Frag8Bf16 frag;
+  __device__ static void read(frag& f, const char* p) {
+    f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  }
+};
+template <> struct LdsFrag<fp8_t> {
+  typedef Frag8Bf16 frag;
+  __device__ static void read(frag& f, const char* p) { fp8x8_to_frag(f, *reinterpret_cast<const u32x2*>(p)); }
+};
+template <> struct LdsFrag<float> {
+  typedef Frag8F32 frag;
+  __device__ static void read(frag& f, const char* p) { load_frag(f, reinterpret_cast<const float*>(p)); }
+};
+
+template <typename TA, typename TW, int RT, int RM, int NSG>
+struct GemmTile {
+  typedef typename LdsFrag<TW>::frag WFr;
+  typedef typename FragOf<TA>::type XFr;
+  static constexpr int GB = 256;                   // bytes per row per group
+  static constexpr int GK = GB / int(sizeof(TW));  // k per group
+  static constexpr int STEPS = GK / 32;            // MFMA k-steps per group
+  static constexpr int SB = 32 * int(sizeof(TW));  // bytes per row per k-step
+  static constexpr int ROWB = GB + 16;             // LDS row stride
+  static constexpr int NLD = 4 * RT;               // load instructions per group
+  static constexpr int LDS_BYTES = 16 * RT * ROWB; // per wave
+
+  // Accumulate rows [n0, n0 + 16 RT) x [m0, m0 + 16 RM) over k in [kb, ke)
+  // (both multiples of 32).  `lds` is this wave's LDS_BYTES region.
+  // Output: lane (r, g) holds acc[i][j][e] = y[row n0 + 16 i + 4 g + e][col m0 + 16 j + r].
+  __device__ static void run(const TA* __restrict__ X, int64_t ldx, const TW* __restrict__ W,
+                             int64_t ldw, int N, int Mact, int n0, int m0, int kb, int ke,
+                             f32x4 (&acc)[RT][RM], char* lds) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int r = lane & 15, g = lane >> 4;   // MFMA roles; for loads: g = row in 4, r = 16-byte piece
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < RM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kb >= ke) return;
+    const int ngroups = (ke - kb + GK - 1) / GK;
+    const int kspan = ke - kb;
+    // load side: instruction j reads row n0 + 4 j + g, bytes [16 r, 16 r + 16) of the group
+    const char* wrow[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      int n = n0 + 4 * j + g;
+      n = n < N ? n : N - 1;
+      wrow[j] = reinterpret_cast<const char*>(W + int64_t(n) * ldw + kb) + 16 * r;
+    }
+    const TA* xrow[RM];
+#pragma unroll
+    for (int j = 0; j < RM; ++j) {
+      int m = m0 + 16 * j + r;
+      m = m < Mact ? m : Mact - 1;
+      xrow[j] = X + int64_t(m) * ldx + kb + 8 * g;
+    }
+    u32x4 wr[NSG][NLD];
+    XFr xr[NSG][STEPS][RM];
+    auto load = [&](int s, int grp) {
+      const int kg = grp * GK;
+      // a 16-byte piece past the end of the K range is never multiplied; read
+      // the group's first piece instead so the address stays inside the row
+      const int off = (kg + (16 * (r + 1)) / int(sizeof(TW)) <= kspan ? kg * int(sizeof(TW)) : -16 * r);
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        wr[s][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + off));
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        const int kk = kg + 32 * st;
+        const int kx = kk < kspan ? kk : 0;
+#pragma unroll
+        for (int j = 0; j < RM; ++j) load_frag(xr[s][st][j], xrow[j] + kx);
+      }
+    };
+    auto compute = [&](int s, int grp) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        *reinterpret_cast<u32x4*>(lds + (4 * j + g) * ROWB + 16 * r) = wr[s][j];
+      __builtin_amdgcn_wave_barrier();
+      const int kg = grp * GK;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        if (kg + 32 * st < kspan) {
+#pragma unroll
+          for (int i = 0; i < RT; ++i) {
+            WFr a;
+            LdsFrag<TW>::read(a, lds + (16 * i + r) * ROWB + st * SB + g * (SB / 4));
+#pragma unroll
+            for (int j = 0; j < RM; ++j) acc[i][j] = mfma_k32(a, xr[s][st][j], acc[i][j]);
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+#pragma unroll
+    for (int s = 0; s < NSG; ++s)
+      if (s < ngroups) load(s, s);
+    int base = 0;
+    for (; base + 2 * NSG <= ngroups; base += NSG) {
+#pragma unroll
+      for (int s = 0; s < NSG; ++s) {
+        compute(s, base + s);
+        // keep the scheduler from hoisting later loads above this stage's
+        // math (that would need a second copy of the register ring)
+        __builtin_amdgcn_sched_barrier(0);
+        load(s, base + NSG + s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSG; ++s) {
+      if (base + s < ngroups) {
+        compute(s, base + s);
+        if (base + s + NSG < ngroups) load(s, base + s + NSG);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSG; ++s)
+      if (base + NSG + s < ngroups) compute(s, base + NSG + s);
+  }
+};
+
+// 1 / rms of an activation row from its per-column-block sums of squares
+// (written by the residual/convolution kernel): the RMSNorm scale, applied
+// to the GEMM result because it is one factor per row.
+__device__ __forceinline__ float row_inv_rms(const RowScale& rs, int m) {
+  if (!rs.sumsq) return 1.f;
+  float s = 0.f;
+  for (int c = 0; c < rs.blocks; ++c) s += rs.sumsq[int64_t(m) * rs.blocks + c];
+  return 1.0f / sqrtf(s * rs.inv_width + rs.eps);
+}
+
+// Partial-sum GEMM.  grid = (ceil(N / (64 RT)), ceil(M / (16 RM)), S).
+template <typename TA, typename TW, int RT, int RM, int NSG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_xwt_kernel(GemmArgs p) {
+  typedef GemmTile<TA, TW, RT, RM, NSG> Tile;
+  __shared__ __attribute__((aligned(16))) char lds[4][Tile::LDS_BYTES];
+  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
+  const int wave = threadIdx.x / WAVE;
+  const int n0 = (blockIdx.x * 4 + wave) * 16 * RT;
+  const int m0 = blockIdx.y * 16 * RM;
+  if (m0 >= Mact || n0 >= p.N) return;
+  const int kb = blockIdx.z * p.k_split;
+  const int ke = min(p.K, kb + p.k_split);
+  f32x4 acc[RT][RM];
+  Tile::run(static_cast<const TA*>(p.X), p.ldx, static_cast<const TW*>(p.W), p.ldw, p.N, Mact, n0, m0,
+            kb, ke, acc, lds[wave]);
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int r = lane & 15, g = lane >> 4;
+  float* P = p.P + int64_t(blockIdx.z) * p.split_stride;
+  float inv[RM];
+#pragma unroll
+  for (int j = 0; j < RM; ++j) inv[j] = row_inv_rms(p.rs, min(m0 + 16 * j + r, Mact - 1));
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int nb = n0 + 16 * i + 4 * g;
+    float s[4] = {1.f, 1.f, 1.f, 1.f};
+    if (p.scale) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] = p.scale[min(nb + e, p.N - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < RM; ++j) {
+      const int m = m0 + 16 * j + r;
+      if (m >= Mact) continue;
+      float* dst = P + int64_t(m) * p.ldp + nb;
+      f32x4 v = acc[i][j];
+      v[0] *= s[0] * inv[j]; v[1] *= s[1] * inv[j]; v[2] *= s[2] * inv[j]; v[3] *= s[3] * inv[j];
+      if (nb + 3 < p.N && (p.ldp & 3) == 0) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nb + e < p.N) dst[e] = v[e];
+      }
+    }
+  }
+}
+
+// lm_head with the per-vocabulary-group top-k fused into the epilogue.
+// grid = (ceil(V / 256), ceil(M / 16)); each block computes the logits of 256
+// vocabulary rows for 16 activation rows over the full K, stages them in LDS,
+// and keeps each activation row's k best (value desc, id asc) as 64-bit keys.
+template <typename TA, typename TW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lmhead_topk_kernel(LmHeadArgs p) {
+  constexpr int RT = 2;  // two passes of 32 rows per wave: 64 rows, 256 per block
+  typedef GemmTile<TA, TW, RT, 1, 2> Tile;
+  __shared__ __attribute__((aligned(16))) char lds[4][Tile::LDS_BYTES];
+  __shared__ float logits[16][256 + 4];
+  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
+  const int m0 = blockIdx.y * 16;
+  if (m0 >= Mact) return;
+  const int wave = threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int r = lane & 15, g = lane >> 4;
+  const int vbase = blockIdx.x * 256;
+  f32x4 acc[2 * RT][1];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int n0 = vbase + wave * 64 + pass * 16 * RT;
+    f32x4 part[RT][1];
+    if (n0 < p.N) {
+      Tile::run(static_cast<const TA*>(p.X), p.ldx, static_cast<const TW*>(p.W), p.ldw, p.N, Mact, n0, m0,
+                0, p.K, part, lds[wave]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) part[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) acc[pass * RT + i][0] = part[i][0];
+  }
+  const float inv = row_inv_rms(p.rs, min(m0 + r, Mact - 1));
+#pragma unroll
+  for (int i = 0; i < 2 * RT; ++i) {
+    const int nl = wave * 64 + 16 * i + 4 * g;  // local vocab index
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n = vbase + nl + e;
+      float v = acc[i][0][e];
+      if (p.scale) v *= p.scale[min(n, p.N - 1)];
+      v *= inv;
+      v = v + 0.0f;
+      logits[r][nl + e] = v;
+      const int m = m0 + r;
+      if (p.debug_logits && n < p.N && m < Mact) p.debug_logits[int64_t(m) * p.N + n] = v;
+    }
+  }
+  __syncthreads();
+  // each wave ranks 4 of the 16 rows
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = wave * 4 + rr;
+    const int m = m0 + row;
+    if (m >= Mact) break;
+    uint64_t key[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int nl = lane + 64 * e;
+      const int n = vbase + nl;
+      key[e] = n < p.N ? rank_key(logits[row][nl], uint32_t(n)) : 0ull;
+    }
+    uint64_t* out = p.cand + (int64_t(m) * p.groups + blockIdx.x) * p.k;
+    for (int t = 0; t < p.k; ++t) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int e = 1; e < 4; ++e) best = key[e] > best ? key[e] : best;
+      best = wave_max_u64(best);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (key[e] == best) key[e] = 0ull;
+      if (lane == 0) out[t] = best;
+    }
+  }
+}
+
+// Final top-k over the per-group candidates of one row, then the logit
+// transform.  grid = (M), block = 256.  Candidates are staged in LDS when
+// they fit (use_lds); each round takes the largest key below the previous
+// one (keys are distinct because ids are).
+__global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p, int use_lds) {
+  extern __shared__ uint64_t cl[];
+  __shared__ uint64_t red[4];
+  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
+  const int m = blockIdx.x;
+  if (m >= Mact) return;
+  const uint64_t* c = p.cand + int64_t(m) * p.count;
+  if (use_lds) {
+    constexpr int U = 8;
+    for (int i0 = threadIdx.x; i0 < p.count; i0 += U * blockDim.x) {
+      uint64_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * blockDim.x;
+        v[u] = i < p.count ? c[i] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * blockDim.x;
+        if (i < p.count) cl[i] = v[u];
+      }
+    }
+    __syncthreads();
+    c = cl;
+  }
+  uint64_t prev = ~0ull;
+  for (int t = 0; t < p.k; ++t) {
+    uint64_t best = 0ull;
+#pragma unroll 8
+    for (int i = threadIdx.x; i < p.count; i += blockDim.x) {
+      const uint64_t v = c[i];
+      best = (v < prev && v > best) ? v : best;
+    }
+    best = wave_max_u64(best);
+    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = best;
+    __syncthreads();
+    best = red[0];
+    for (int w = 1; w < int(blockDim.x / WAVE); ++w) best = red[w] > best ? red[w] : best;
+    __syncthreads();
+    prev = best;
+    if (threadIdx.x == 0) {
+      float z = p.multiplier * key_val(best);
+      if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
+      p.ids[int64_t(m) * p.k + t] = int32_t(key_id(best));
+      p.vals[int64_t(m) * p.k + t] = z;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+// ---------------------------------------------------------------------------
+template <typename TA, typename TW, int RT, int RM, int NSG>
+static void launch_gemm_t(const GemmArgs& a, hipStream_t s) {
+  dim3 grid((a.N + 64 * RT - 1) / (64 * RT), (a.M + 16 * RM - 1) / (16 * RM), a.splits);
+  hipLaunchKernelGGL((gemm_xwt_kernel<TA, TW, RT, RM, NSG>), grid, dim3(256), 0, s, a);
+}
+
+// 32 weight rows per wave (128 per block); two groups in flight for up to 16
+// activation rows, one when a group carries more activation fragments.
+template <typename TA, typename TW>
+static void launch_gemm_rm(const GemmArgs& a, hipStream_t s) {
+  constexpr int NSG1 = sizeof(TW) == 1 ? 1 : 2;  // fp8 groups carry twice the activation fragments
+  if (a.M <= 16) launch_gemm_t<TA, TW, 2, 1, NSG1>(a, s);
+  else if (a.M <= 32) launch_gemm_t<TA, TW, 2, 2, 1>(a, s);
+  else launch_gemm_t<TA, TW, 2, 4, 1>(a, s);
+}
+
+int gemm_rows_per_block(int weight_dtype, int M) {
+  (void)weight_dtype;
+  (void)M;
+  return 128;
+}
+
+void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s) {
+  switch (weight_dtype) {
+    case 0: launch_gemm_rm<float, float>(a, s); break;
+    case 1: launch_gemm_rm<bf16_t, bf16_t>(a, s); break;
+    default: launch_gemm_rm<bf16_t, fp8_t>(a, s); break;
+  }
+}
+
+void launch_lmhead_topk(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
+  dim3 grid(a.groups, (a.M + 15) / 16);
+  switch (weight_dtype) {
+    case 0: hipLaunchKernelGGL((lmhead_topk_kernel<float, float>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((lmhead_topk_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((lmhead_topk_kernel<bf16_t, fp8_t>), grid, dim3(256), 0, s, a); break;
+  }
+}
+
+void launch_topk_merge(const TopkMergeArgs& a, hipStream_t s) {
+  const size_t lds = size_t(a.count) * 8;
+  const int use_lds = lds <= 64 * 1024 ? 1 : 0;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(a.M), dim3(256), use_lds ? lds : 0, s, a, use_lds);
+}
+
+}  // namespace dfl

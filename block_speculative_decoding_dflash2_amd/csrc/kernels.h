@@ -1,0 +1,145 @@
+// Kernel argument blocks and host launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+// Per-row RMSNorm factor applied in a GEMM epilogue: row m is multiplied by
+// 1 / sqrt(sum_c sumsq[m][c] * inv_width + eps).  sumsq == null: factor 1.
+struct RowScale {
+  const float* sumsq; int blocks; float inv_width; float eps;
+};
+
+// y[s][m][n] = rowscale[m] * sum_{k in split s} X[m][k] * W[n][k]  (* scale[n])
+struct GemmArgs {
+  const void* X; int64_t ldx;     // [M][K] act
+  const void* W; int64_t ldw;     // [N][K] weight
+  const float* scale;             // [N] or null
+  float* P; int64_t ldp;          // [splits][M][ldp] float32
+  int64_t split_stride;           // elements between splits
+  int M, N, K;                    // M = upper bound on rows
+  const int32_t* M_dev;           // actual rows = min(*M_dev, M) if set
+  int splits, k_split;            // K range per split (multiple of 32)
+  RowScale rs;
+};
+
+struct LmHeadArgs {
+  const void* X; int64_t ldx;     // [M][K] act
+  const void* W; int64_t ldw;     // [V][K]
+  const float* scale;             // [V] or null
+  int M, N, K;                    // N = vocab
+  const int32_t* M_dev;
+  int groups;                     // ceil(V / 256)
+  int k;                          // candidates per group and row
+  uint64_t* cand;                 // [M][groups][k] ranking keys
+  float* debug_logits;            // [M][V] or null
+  RowScale rs;
+};
+
+struct TopkMergeArgs {
+  const uint64_t* cand;           // [M][count]
+  int count, M, k;
+  const int32_t* M_dev;
+  int32_t* ids; float* vals;      // [M][k]
+  float multiplier, softcap;
+};
+
+// Residual / embedding + optional in-block convolution; writes the new
+// residual, gain * residual in act dtype and per-column-block sums of squares
+// (the RMSNorm factor is applied by the consuming GEMM).
+struct NormArgs {
+  int H;
+  int rows;                       // upper bound on rows
+  const int32_t* rows_dev;        // actual rows if set
+  int bs;                         // rows per block (conv boundary; 1 = no neighbours)
+  // input: embedding mode (embed != null) or residual mode
+  const void* embed; const int32_t* anchors; int mask_id; int vocab; float emb_scale;
+  const float* base;              // [rows][H] or null
+  const float* parts; int splits; int64_t split_stride; int64_t ldp;  // partial sums
+  const void* conv; int conv_k;   // [conv_k][H] param or null
+  const void* gain;
+  float* h_out;                   // [rows][H] float32 or null
+  void* n_out;                    // act [out rows][H]: gain * y; row map below
+  float* sumsq;                   // [out rows][col_blocks] sums of y^2
+  int t_first;                    // slots t < t_first produce no n_out / sumsq row
+};
+
+struct QkvEpiArgs {
+  const float* parts; int splits; int64_t split_stride; int64_t ldp;  // [S][M][(nq+2nkv)d]
+  const int32_t* ctx_lens;
+  int M, bs, nq, nkv, d, Lmax;
+  float theta;
+  void* q_out;                    // [M][nq][d] act
+  void* k_layer; void* v_layer;   // cache base of this layer: [Bcap][nkv][Lmax][d], [Bcap][nkv][d][Lmax]
+};
+
+struct KvAppendArgs {
+  const float* parts; int splits; int64_t split_stride; int64_t ldp;  // per layer [S][Mn][2 nkv d]
+  int64_t layer_stride;           // elements between layers' partial blocks
+  const int32_t* offsets;         // [B + 1]
+  const int32_t* ctx_lens;        // [B]
+  int B, Mn, nkv, d, Lmax, nL;
+  int64_t cache_layer_stride;     // elements per layer in the caches
+  float theta;
+  void* k_cache; void* v_cache;
+};
+
+struct SwigluArgs {
+  const float* parts; int splits; int64_t split_stride; int64_t ldp;  // [S][M][2F]
+  int M, F;
+  void* out;                      // [M][F] act
+};
+
+struct AttnArgs {
+  const void* q;                  // [B*bs][nq][d] act
+  const void* k_layer; const void* v_layer;
+  const int32_t* ctx_lens;
+  int B, bs, nq, nkv, d, Lmax, window;
+  int chunk_keys, nchunks, qgroups;   // keys per block (multiple of the sub-chunk)
+  float* part_o;                  // [B][nkv][nchunks][QS][d]
+  float* part_ml;                 // [B][nkv][nchunks][QS][2]
+  float scale_log2;
+};
+
+struct AttnCombineArgs {
+  const float* part_o; const float* part_ml;
+  const int32_t* ctx_lens;
+  int B, bs, nq, nkv, d, Lmax, window, chunk_keys, nchunks;
+  void* o;                        // [B*bs][nq*d] act
+};
+
+struct SelectArgs {
+  const int32_t* anchors; const int32_t* ids; const float* vals;
+  const float* tl; const float* tr;
+  int B, P, k, r, V;
+  int32_t* path; int32_t* drafts; float* score; float* debug_pair;
+};
+
+struct VerifyArgs {
+  const int32_t* drafts; const float* logits;
+  int B, bs, V, nchunks, chunk;
+  uint64_t* part;                 // [B*bs][nchunks]
+  int32_t* accepted; int32_t* bonus; int32_t* argmax;
+};
+
+int gemm_rows_per_block(int weight_dtype, int M);
+void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s);
+void launch_lmhead_topk(int weight_dtype, const LmHeadArgs& a, hipStream_t s);
+void launch_topk_merge(const TopkMergeArgs& a, hipStream_t s);
+int norm_col_blocks(int H);
+void launch_norm(bool f32, const NormArgs& a, hipStream_t s);
+void launch_qkv_epilogue(bool f32, const QkvEpiArgs& a, hipStream_t s);
+void launch_kv_append(bool f32, const KvAppendArgs& a, hipStream_t s);
+void launch_swiglu(bool f32, const SwigluArgs& a, hipStream_t s);
+bool attn_supported(int d);
+int attn_sub_chunk(bool f32, int d);
+void launch_attention(bool f32, const AttnArgs& a, hipStream_t s);
+void launch_attn_combine(bool f32, const AttnCombineArgs& a, hipStream_t s);
+__host__ __device__ int select_row_stride(int r);
+void launch_select(const SelectArgs& a, size_t lds_bytes, hipStream_t s);
+void launch_verify_partial(const VerifyArgs& a, hipStream_t s);
+void launch_verify_final(const VerifyArgs& a, hipStream_t s);
+
+}  // namespace dfl

@@ -1,0 +1,274 @@
+/*
+ * dflash2.h -- C ABI of the DFlash2 block draft -> select -> verify step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The step (per sequence):
+ *   1. append the target hidden-state taps of newly verified positions to the
+ *      draft's context (feature projection + RMSNorm, then every layer's
+ *      key/value projection with RoPE) -- NeMo AutoModel, "Train a DFlash
+ *      Drafter for Speculative Decoding", section "What is DFlash?";
+ *   2. run one non-causal forward of the draft stack over a block of
+ *      block_size slots (slot 0 = the real anchor token, the rest = the
+ *      reserved mask id), with a two-tap in-block depthwise convolution before
+ *      every sublayer -- same page, sections "What is DFlash?" and "Variants"
+ *      (row "DFlash 2"), and "Data" (mask token);
+ *   3. project slots 1..block_size-1 through the shared lm_head and keep the
+ *      selector_top_k best candidates per slot -- same page, "Variants";
+ *   4. pick one coherent path through the candidate lattice with a rank-r
+ *      pairwise selector solved by max-sum dynamic programming -- same page,
+ *      "Variants" and "Objective"; llama-cpp-python wiki "DFlash2 Speculative
+ *      Decoding", "Complete Runnable Code" (selector lattice);
+ *   5. verify the path greedily against the target's logits and return the
+ *      longest accepted prefix plus the target's own next token -- NeMo
+ *      SpeechLM "DFlash speculative decoding with vLLM", intro and
+ *      "Validation"; llama-cpp-python wiki, "Prerequisites".
+ *
+ * Conventions for every call:
+ *   - Pointers marked [device] are device addresses on the current HIP
+ *     device; [host] are host addresses.  The library never allocates device
+ *     memory and never synchronises: work is enqueued on `stream` and the call
+ *     returns.  The caller owns every buffer and must keep inputs alive and
+ *     outputs unread until the stream reaches the enqueued work.
+ *   - All linear weights are row-major [out, in]: y = x * W^T.
+ *   - Element types: "act" is float32 when config.weight_dtype == FP32 and
+ *     bf16 (uint16 bit pattern) otherwise; "param" (embedding, conv taps,
+ *     norm gains) follows act; weights of the linears follow weight_dtype
+ *     (fp8 = OCP e4m3fn codes with one float32 scale per output row).
+ *   - Every call returns DFLASH2_OK or an error code; on error nothing was
+ *     enqueued and dflash2_last_error() (thread-local) describes it.  Device
+ *     data (ids, lengths, offsets) cannot be checked on the host; kernels
+ *     skip any access such data would push outside its buffer, so a bad
+ *     value gives wrong results for that sequence, never a fault.
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH2_OK = 0,
+  DFLASH2_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum   */
+  DFLASH2_ERR_SHAPE = 2,       /* sizes inconsistent with the handle       */
+  DFLASH2_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. K % 32)  */
+  DFLASH2_ERR_WORKSPACE = 4,   /* workspace null, misaligned or too small  */
+  DFLASH2_ERR_HIP = 5          /* a HIP runtime call failed                */
+} dflash2_status;
+
+typedef enum { DFLASH2_FP32 = 0, DFLASH2_BF16 = 1, DFLASH2_FP8_E4M3 = 2 } dflash2_dtype;
+
+/* Draft configuration.  Field names follow the dflash_config keys (NeMo
+ * SpeechLM page, "DFlash2 inference") and the recipe keys (NeMo AutoModel
+ * page, "Key Config Fields" table).  target_layer_ids enter only through
+ * num_taps and the order of the taps in new_taps. */
+typedef struct {
+  int32_t hidden;           /* draft width H                                  */
+  int32_t num_layers;       /* draft_num_hidden_layers                        */
+  int32_t num_q_heads;      /* draft_num_attention_heads                      */
+  int32_t num_kv_heads;     /* draft_num_key_value_heads (divides num_q_heads) */
+  int32_t head_dim;         /* draft_head_dim (even, <= 256)                  */
+  int32_t ffn;              /* SwiGLU width F                                 */
+  int32_t vocab;            /* V, shared with the target                      */
+  int32_t num_taps;         /* len(target_layer_ids)                          */
+  int32_t tap_width;        /* target hidden width of one tap                 */
+  int32_t block_size;       /* num_speculative_tokens + 1, >= 2               */
+  int32_t conv_kernel_size; /* taps of the in-block convolution, 1..block_size */
+  int32_t selector_top_k;   /* candidates per slot, 1..64, <= vocab           */
+  int32_t selector_rank;    /* rank r of the pairwise selector, 1..256        */
+  int32_t max_batch;        /* sequences a cache holds (its batch dimension)  */
+  int32_t max_context;      /* rows a cache holds per sequence and kv head    */
+  int32_t sliding_window;   /* draft_sliding_window; 0 = attend to all rows   */
+  int32_t mask_token_id;    /* reserved id filling slots 1..block_size-1      */
+  int32_t weight_dtype;     /* dflash2_dtype of the linears and lm_head       */
+  float rms_eps;            /* RMSNorm epsilon                                */
+  float rope_theta;         /* RoPE base                                      */
+  float input_embedding_scale;   /* scales the embedded block (1 = identity)  */
+  float output_multiplier;       /* logit transform multiplier (1 = identity) */
+  float final_logit_softcapping; /* logit soft cap; 0 = off                   */
+} dflash2_config;
+
+/* Per-layer weights [device].  *_scale are float32 [out rows], required for
+ * FP8_E4M3 and ignored otherwise. */
+typedef struct {
+  const void* conv_attn;     /* [conv_kernel_size, H] param: tap j multiplies slot t-j */
+  const void* attn_norm;     /* [H] param                                     */
+  const void* wqkv;          /* [(nq + 2 nkv) * d, H]: q heads, k heads, v heads */
+  const float* wqkv_scale;
+  const void* wo;            /* [H, nq * d]                                   */
+  const float* wo_scale;
+  const void* conv_ffn;      /* [conv_kernel_size, H] param                   */
+  const void* ffn_norm;      /* [H] param                                     */
+  const void* w_gate_up;     /* [2F, H]: rows 0..F-1 gate, F..2F-1 up         */
+  const float* w_gate_up_scale;
+  const void* w_down;        /* [H, F]                                        */
+  const float* w_down_scale;
+} dflash2_layer_weights;
+
+/* Draft weights.  Device pointers, not owned: they must outlive the handle.
+ * `layers` is a [host] array of num_layers entries, copied at create. */
+typedef struct {
+  const void* embed;         /* [V, H] param: the target's embed_tokens       */
+  const void* lm_head;       /* [V, H] weight dtype: the target's lm_head     */
+  const float* lm_head_scale;
+  const void* proj;          /* [H, num_taps * tap_width] feature projection  */
+  const float* proj_scale;
+  const void* proj_norm;     /* [H] param                                     */
+  const void* final_norm;    /* [H] param                                     */
+  const float* sel_tl;       /* [V, r] float32 left selector factors          */
+  const float* sel_tr;       /* [V, r] float32 right selector factors         */
+  const dflash2_layer_weights* layers;
+} dflash2_weights;
+
+typedef struct dflash2_handle dflash2_handle;
+
+/* Validate the configuration and weight table and build a handle.  Rejects
+ * (before any device work, the same rule the NIM page states for draft heads
+ * in "Bring Your Own DFlash2 Head"): block_size < 2, num_q_heads not a
+ * multiple of num_kv_heads, odd or oversized head_dim, conv_kernel_size
+ * outside 1..block_size, selector_top_k outside 1..min(64, vocab),
+ * selector_rank outside 1..256, mask_token_id outside [0, vocab), an unknown
+ * weight_dtype, a null weight, a missing fp8 scale, and (UNSUPPORTED) any
+ * contraction length (hidden, ffn, nq*head_dim, num_taps*tap_width) that is
+ * not a multiple of 32.  The handle keeps a host copy of the config and the
+ * pointer table only; it is immutable and may be shared across threads and
+ * streams. */
+dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weights* weights,
+                              dflash2_handle** out);
+void dflash2_destroy(dflash2_handle* handle);
+
+/* Bytes of device workspace dflash2_draft_block needs for `batch` sequences
+ * and at most `max_new_rows` appended context rows in total. */
+dflash2_status dflash2_workspace_size(const dflash2_handle* handle, int32_t batch,
+                                      int64_t max_new_rows, size_t* bytes);
+
+/* Steps 1-3 for `batch` sequences (1 <= batch <= max_batch).
+ *   anchor_ids  [device] int32 [batch]: the last verified token of each
+ *               sequence; it fills slot 0.
+ *   new_taps    [device] act [max_new_rows, num_taps, tap_width]: target
+ *               hidden states of the newly verified positions, sequence by
+ *               sequence, taps in target_layer_ids order.
+ *   new_offsets [device] int32 [batch + 1]: prefix sums of the rows each
+ *               sequence appends; new_offsets[batch] <= max_new_rows.
+ *   ctx_lens    [device] int32 [batch]: context length L_b after the append;
+ *               the new rows take positions L_b - n_b .. L_b - 1 and the
+ *               block's slots positions L_b .. L_b + block_size - 1, so
+ *               L_b + block_size <= max_context is required.
+ *   max_new_rows [host]: upper bound on new_offsets[batch] (sizes grids and
+ *               the workspace; block_size * batch bounds a warm step).
+ *   k_cache     [device] act [num_layers][max_batch][num_kv_heads][max_context][head_dim]
+ *   v_cache     [device] act [num_layers][max_batch][num_kv_heads][head_dim][max_context]
+ *               (values are stored transposed: position is the fastest axis).
+ *               Keys are stored after RoPE.  The call writes context rows
+ *               [L_b - n_b, L_b) and uses rows [L_b, L_b + block_size) as
+ *               scratch for the block's own keys/values; nothing else.  A
+ *               rejected block therefore needs no rollback: the next step's
+ *               append overwrites the scratch rows it reaches.
+ *   topk_ids    [device] int32 [batch, block_size-1, selector_top_k]: per slot
+ *               1.. the best ids under (logit desc, id asc), -0.0 ranked as +0.0.
+ *   topk_vals   [device] float [batch, block_size-1, selector_top_k]: the
+ *               logit transform applied to those logits.
+ *   debug_logits [device, nullable] float [batch, block_size-1, vocab]: the
+ *               float32 logits the ranking used (before the transform).
+ *   debug_hidden [device, nullable] float [batch, block_size, hidden]: the
+ *               residual stream after the last layer.
+ *   workspace   [device] >= dflash2_workspace_size bytes, 256-byte aligned;
+ *               scratch only, contents need no initialisation. */
+dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                   const int32_t* anchor_ids, const void* new_taps,
+                                   const int32_t* new_offsets, const int32_t* ctx_lens,
+                                   int64_t max_new_rows, void* k_cache, void* v_cache,
+                                   int32_t* topk_ids, float* topk_vals, float* debug_logits,
+                                   float* debug_hidden, void* workspace, size_t workspace_bytes);
+
+/* Step 4.  One coherent path per sequence through the candidate lattice:
+ *   c_0 = anchor, c_t = topk_ids[b, t-1, path_t], maximising
+ *   sum_t pi(c_{t-1}, c_t) + topk_vals[b, t-1, path_t]  with
+ *   pi(a, b) = sum_m sel_tl[a, m] * sel_tr[b, m]
+ * evaluated in float32 exactly as: multiply, then add, m ascending from +0;
+ * S_1 = pi(c_0, .) + z_1; S_t = max_i (S_{t-1}[i] + pi) + z_t.  Ties take
+ * the smallest predecessor rank and the smallest final rank.
+ *   anchor_ids [device] int32 [batch]; topk_ids/topk_vals as produced above
+ *   (any candidates may be passed: ids are only used to index the tables).
+ *   path_idx   [device] int32 [batch, block_size-1]: chosen candidate rank.
+ *   draft_tokens [device] int32 [batch, block_size-1]: chosen token ids.
+ *   path_score [device, nullable] float [batch].
+ *   debug_pair [device, nullable] float [batch, block_size-1, k, k]: pair
+ *              scores pi(c_{t-1,i}, c_{t,j}); slab 0 repeats pi(anchor, c_{1,j})
+ *              in every row i.
+ * No workspace; 1 <= batch <= max_batch. */
+dflash2_status dflash2_select_path(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                   const int32_t* anchor_ids, const int32_t* topk_ids,
+                                   const float* topk_vals, int32_t* path_idx,
+                                   int32_t* draft_tokens, float* path_score, float* debug_pair);
+
+/* Bytes of device workspace dflash2_verify_accept needs. */
+dflash2_status dflash2_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
+                                             size_t* bytes);
+
+/* Step 5, stateless.  Row i of target_logits [device] float [batch,
+ * block_size, vocab] is the target's prediction after block slot i (slot 0 =
+ * the anchor).  g_i = argmax (ties to the smallest id, -0.0 as +0.0, NaN
+ * never wins).  accepted[b] = the largest n <= block_size-1 with
+ * g_i == draft_tokens[b, i] for all i < n; bonus[b] = g_n.  The step emits
+ * accepted[b] drafts plus the bonus token.
+ *   draft_tokens [device] int32 [batch, block_size-1]
+ *   accepted, bonus [device] int32 [batch]
+ *   target_argmax [device, nullable] int32 [batch, block_size]
+ *   workspace [device] >= dflash2_verify_workspace_size bytes, 256-aligned. */
+dflash2_status dflash2_verify_accept(hipStream_t stream, int32_t batch, int32_t block_size,
+                                     int32_t vocab, const int32_t* draft_tokens,
+                                     const float* target_logits, int32_t* accepted,
+                                     int32_t* bonus, int32_t* target_argmax, void* workspace,
+                                     size_t workspace_bytes);
+
+/* Optional per-kernel timing (instrumentation for benchmarks and profiling).
+ * While a trace is attached on a thread, every kernel that calls from this
+ * thread enqueue is bracketed by hipEventRecord(entry.start / entry.stop) on
+ * the call's stream, and the entry receives the kernel kind and its
+ * algorithmic traffic and work: bytes = every input read once plus every
+ * output written once (split-K partial sums and other scratch excluded;
+ * appended rows and context lengths counted at their host-side bounds),
+ * flops = multiply-adds x 2.  The caller creates the events (hipEventCreate)
+ * and reads them after synchronising.  At most `capacity` launches are
+ * recorded; later launches run untraced. */
+typedef enum {
+  DFLASH2_K_GEMM = 0,         /* weight-streaming linear (draft linears, projections) */
+  DFLASH2_K_LMHEAD_TOPK = 1,  /* lm_head with the fused per-group top-k      */
+  DFLASH2_K_TOPK_MERGE = 2,
+  DFLASH2_K_NORM = 3,         /* residual + conv + RMSNorm                   */
+  DFLASH2_K_QKV_EPILOGUE = 4,
+  DFLASH2_K_KV_APPEND = 5,
+  DFLASH2_K_SWIGLU = 6,
+  DFLASH2_K_ATTENTION = 7,
+  DFLASH2_K_ATTN_COMBINE = 8,
+  DFLASH2_K_SELECT = 9,
+  DFLASH2_K_VERIFY_PARTIAL = 10,
+  DFLASH2_K_VERIFY_FINAL = 11
+} dflash2_kernel_kind;
+
+typedef struct {
+  hipEvent_t start, stop;     /* [host] created by the caller               */
+  int32_t kind;               /* dflash2_kernel_kind, filled by the library */
+  int32_t reserved;
+  int64_t bytes;              /* algorithmic bytes of this launch           */
+  int64_t flops;              /* algorithmic flops of this launch           */
+} dflash2_trace_entry;
+
+/* Attach [host] entries[capacity] to the calling thread (replaces any
+ * attached trace).  Not for use while another call on this thread runs. */
+dflash2_status dflash2_trace_attach(dflash2_trace_entry* entries, int32_t capacity);
+/* Detach; returns the number of entries filled (<= capacity). */
+int32_t dflash2_trace_detach(void);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* dflash2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH2_H */

@@ -72,8 +72,24 @@ class Workload:
 
     @property
     def max_context(self) -> int:
-        # rows [ctx, ctx + block_size) hold the block's transient keys/values
-        return self.ctx[1] + self.block_size
+        # rows [ctx, ctx + block_size) hold the block's transient keys/values;
+        # rounded up to a multiple of 32 rows
+        return (self.ctx[1] + self.block_size + 31) // 32 * 32
+
+    def abi_config(self) -> dict:
+        """Field values of the C ABI's dflash2_config for this workload."""
+        return dict(
+            hidden=self.hidden, num_layers=self.num_layers, num_q_heads=self.num_q_heads,
+            num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, ffn=self.ffn,
+            vocab=self.vocab, num_taps=self.num_taps, tap_width=self.tap_width,
+            block_size=self.block_size, conv_kernel_size=self.conv_kernel_size,
+            selector_top_k=self.top_k, selector_rank=self.rank, max_batch=self.batch,
+            max_context=self.max_context, sliding_window=self.sliding_window,
+            mask_token_id=self.mask_token_id, weight_dtype=self.weight_dtype,
+            rms_eps=self.rms_eps, rope_theta=self.rope_theta,
+            input_embedding_scale=self.input_embedding_scale,
+            output_multiplier=self.output_multiplier,
+            final_logit_softcapping=self.final_logit_softcapping)
 
     def agreement(self, pos: int) -> float:
         """Probability that the verifier agrees with the draft at block position pos (1-based)."""

@@ -170,17 +170,24 @@ def make_weights(w: Workload) -> Weights:
             w_gate_up=encode(normal((2 * w.ffn, H), t(L_WGU), sd), wd),
             w_down=encode(normal((H, w.ffn), t(L_WDOWN), sd), wd),
         ))
-    tstd = w.selector_table_std()
+    tl, tr = make_selector_tables(w)
     return Weights(
         embed=encode(normal((V, H), (w.index, T_EMBED), sd), pd),
         lm_head=encode(normal((V, H), (w.index, T_LMHEAD), sd), wd),
         proj=encode(normal((H, w.num_taps * w.tap_width), (w.index, T_PROJ), sd), wd),
         proj_norm=_gain(w, T_PROJ_NORM, H),
         final_norm=_gain(w, T_FINAL_NORM, H),
-        sel_tl=encode(normal((V, w.rank), (w.index, T_SEL_L), tstd), "fp32"),
-        sel_tr=encode(normal((V, w.rank), (w.index, T_SEL_R), tstd), "fp32"),
+        sel_tl=encode(tl, "fp32"),
+        sel_tr=encode(tr, "fp32"),
         layers=layers,
     )
+
+
+def make_selector_tables(w: Workload):
+    """Left and right selector factor tables [V, r] float32."""
+    tstd = w.selector_table_std()
+    return (normal((w.vocab, w.rank), (w.index, T_SEL_L), tstd),
+            normal((w.vocab, w.rank), (w.index, T_SEL_R), tstd))
 
 
 def accepted_draws(w: Workload, n: int, seed_key) -> np.ndarray:

@@ -1,0 +1,175 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point
+include/dflash2.h declares, and rejects bad arguments before any HIP call
+(every case here runs without a GPU).  Also the acceptance-metrics record
+against the hand-worked fixture."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_speculative_decoding_dflash2_amd as pkg
+from block_speculative_decoding_dflash2_amd import _lib as L
+from block_speculative_decoding_dflash2_amd.runner import config_struct
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash2.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash2_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(L.EXPORTED)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _fake_weights(nl=1, fp8=False):
+    """Non-null placeholder addresses: create() only validates the table."""
+    lw = (L.dflash2_layer_weights * nl)()
+    for i in range(nl):
+        for f, _ in L.dflash2_layer_weights._fields_:
+            if f.endswith("_scale") and not fp8:
+                continue
+            setattr(lw[i], f, 0x1000)
+    w = L.dflash2_weights()
+    for f, _ in L.dflash2_weights._fields_:
+        if f == "layers":
+            continue
+        if f.endswith("_scale") and not fp8:
+            continue
+        setattr(w, f, 0x1000)
+    w.layers = ctypes.cast(lw, ctypes.POINTER(L.dflash2_layer_weights))
+    return w, lw
+
+
+def _status_create(cfg):
+    w, keep = _fake_weights(cfg["num_layers"], cfg["weight_dtype"] == "fp8")
+    h = ctypes.c_void_p()
+    st = L.lib.dflash2_create(ctypes.byref(config_struct(cfg)), ctypes.byref(w), ctypes.byref(h))
+    if st == 0:
+        L.lib.dflash2_destroy(h)
+    return st
+
+
+BASE = synth.get("tiny_fp32").abi_config()
+
+
+@pytest.mark.parametrize("change,status", [
+    ({}, L.DFLASH2_OK),
+    ({"block_size": 1}, L.DFLASH2_ERR_SHAPE),
+    ({"num_q_heads": 6, "num_kv_heads": 4}, L.DFLASH2_ERR_SHAPE),
+    ({"conv_kernel_size": 9}, L.DFLASH2_ERR_SHAPE),
+    ({"conv_kernel_size": 0}, L.DFLASH2_ERR_SHAPE),
+    ({"selector_top_k": 0}, L.DFLASH2_ERR_SHAPE),
+    ({"selector_top_k": 65}, L.DFLASH2_ERR_SHAPE),
+    ({"selector_rank": 0}, L.DFLASH2_ERR_SHAPE),
+    ({"selector_rank": 257}, L.DFLASH2_ERR_SHAPE),
+    ({"mask_token_id": 512}, L.DFLASH2_ERR_SHAPE),
+    ({"weight_dtype": 7}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"hidden": 0}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"head_dim": 24}, L.DFLASH2_ERR_UNSUPPORTED),
+    ({"hidden": 80}, L.DFLASH2_ERR_UNSUPPORTED),
+    ({"max_context": 36}, L.DFLASH2_ERR_UNSUPPORTED),
+    ({"max_context": 4}, L.DFLASH2_ERR_SHAPE),
+    ({"selector_top_k": 64, "selector_rank": 256}, L.DFLASH2_ERR_UNSUPPORTED),
+])
+def test_create_validation(change, status):
+    cfg = dict(BASE, **change)
+    assert _status_create(cfg) == status
+    if status != L.DFLASH2_OK:
+        assert L.dflash2_last_error() != ""
+
+
+def test_create_rejects_null_weights_and_missing_fp8_scales():
+    cfg = dict(BASE)
+    w, keep = _fake_weights(1)
+    w.embed = None
+    h = ctypes.c_void_p()
+    assert L.lib.dflash2_create(ctypes.byref(config_struct(cfg)), ctypes.byref(w), ctypes.byref(h)) \
+        == L.DFLASH2_ERR_INVALID_ARG
+    cfg8 = dict(BASE, weight_dtype="fp8")
+    w8, keep8 = _fake_weights(1, fp8=False)
+    assert L.lib.dflash2_create(ctypes.byref(config_struct(cfg8)), ctypes.byref(w8), ctypes.byref(h)) \
+        == L.DFLASH2_ERR_INVALID_ARG
+    assert "scale" in L.dflash2_last_error()
+
+
+def _handle(cfg):
+    w, keep = _fake_weights(cfg["num_layers"], cfg["weight_dtype"] == "fp8")
+    h = L.dflash2_create(config_struct(cfg), w)
+    return h, (w, keep)
+
+
+def test_workspace_size_and_draft_argument_errors():
+    h, keep = _handle(BASE)
+    try:
+        n1 = L.dflash2_workspace_size(h, 1, 32)
+        n0 = L.dflash2_workspace_size(h, 1, 0)
+        assert n1 > n0 > 0 and n1 % 256 == 0
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_workspace_size(h, 2, 8)          # batch > max_batch
+        assert e.value.status == L.DFLASH2_ERR_SHAPE
+        p = 0x1000
+        # null anchor pointer
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_draft_block(h, None, 1, None, p, p, p, 8, p, p, p, p, None, None, p, n1)
+        assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
+        # workspace too small / misaligned
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_draft_block(h, None, 1, p, p, p, p, 32, p, p, p, p, None, None, p, n1 - 1)
+        assert e.value.status == L.DFLASH2_ERR_WORKSPACE
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_draft_block(h, None, 1, p, p, p, p, 32, p, p, p, p, None, None, p + 8, n1)
+        assert e.value.status == L.DFLASH2_ERR_WORKSPACE
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_draft_block(h, None, 0, p, p, p, p, 32, p, p, p, p, None, None, p, n1)
+        assert e.value.status == L.DFLASH2_ERR_SHAPE
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_select_path(h, None, 1, p, None, p, p, p, None, None)
+        assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_select_path(h, None, 3, p, p, p, p, p, None, None)
+        assert e.value.status == L.DFLASH2_ERR_SHAPE
+    finally:
+        L.dflash2_destroy(h)
+
+
+def test_verify_argument_errors():
+    n = L.dflash2_verify_workspace_size(4, 8, 1000)
+    assert n > 0 and n % 256 == 0
+    p = 0x1000
+    with pytest.raises(L.DFlash2Error) as e:
+        L.dflash2_verify_accept(None, 4, 1, 1000, p, p, p, p, None, p, n)
+    assert e.value.status == L.DFLASH2_ERR_SHAPE
+    with pytest.raises(L.DFlash2Error) as e:
+        L.dflash2_verify_accept(None, 4, 8, 1000, p, None, p, p, None, p, n)
+    assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
+    with pytest.raises(L.DFlash2Error) as e:
+        L.dflash2_verify_accept(None, 4, 8, 1000, p, p, p, p, None, p, n - 8)
+    assert e.value.status == L.DFLASH2_ERR_WORKSPACE
+
+
+def test_full_workload_configs_validate():
+    for name in synth.WORKLOADS:
+        cfg = synth.get(name).abi_config()
+        assert _status_create(cfg) == L.DFLASH2_OK, (name, L.dflash2_last_error())
+    for name in synth.TEST_WORKLOADS:
+        cfg = synth.get(name).abi_config()
+        assert _status_create(cfg) == L.DFLASH2_OK, (name, L.dflash2_last_error())
+
+
+def test_speculative_metrics_fixture():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "metrics_hand.json")))
+    m = pkg.metrics.speculative_metrics(g["per_step_accepted"], g["num_spec_tokens"])
+    for k, v in g["expected"].items():
+        assert m[k] == pytest.approx(v) if isinstance(v, float) else m[k] == v, k
