@@ -2,6 +2,7 @@
 // factors, attention chunking, workspace carve-up) and the launch sequence
 // of one draft step.  No device memory is allocated and no call
 // synchronises; everything is enqueued on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -181,9 +182,7 @@ const void* byte_offset(const void* p, int64_t bytes) {
   return static_cast<const char*>(p) + bytes;
 }
 
-size_t select_lds(int k, int r, int P) {
-  return size_t(2 * k * select_row_stride(r) + k * k + k + P * k) * 4;
-}
+constexpr size_t kSelectLds = 60 * 1024;
 
 }  // namespace
 
@@ -245,7 +244,7 @@ dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weight
   if (c.hidden > 16384) return fail(DFLASH2_ERR_UNSUPPORTED, "create: hidden > 16384");
   if (c.max_context % 8)
     return fail(DFLASH2_ERR_UNSUPPORTED, "create: max_context must be a multiple of 8");
-  if (select_lds(c.selector_top_k, c.selector_rank, c.block_size - 1) > 64 * 1024)
+  if (select_window(c.selector_top_k, c.selector_rank, c.block_size - 1, kSelectLds) < 1)
     return fail(DFLASH2_ERR_UNSUPPORTED, "create: selector_top_k * selector_rank too large");
   const dflash2_weights& w = *weights;
   if (!w.embed || !w.lm_head || !w.proj || !w.proj_norm || !w.final_norm || !w.sel_tl ||
@@ -333,7 +332,7 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
     a.X = X; a.ldx = ldx; a.W = W; a.ldw = K; a.scale = scale;
     a.P = out; a.ldp = N; a.split_stride = int64_t(M) * N;
     a.M = M; a.N = N; a.K = K; a.M_dev = M_dev;
-    a.splits = sp.splits; a.k_split = sp.k_split;
+    a.splits = sp.splits; a.k_split = sp.k_split; a.groups = 1;
     const int64_t bytes = int64_t(N) * K * wb + (scale ? int64_t(N) * 4 : 0) + int64_t(M) * K * ab +
                           int64_t(M) * N * 4;
     traced(stream, DFLASH2_K_GEMM, bytes, 2 * int64_t(M) * N * K, [&] { launch_gemm(dt, a, stream); });
@@ -360,13 +359,27 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
     gemm(new_taps, Kp, handle->w.proj, handle->w.proj_scale, P.Mn, rows_dev, H, Kp, P.proj, parts, plain);
     norm(P.Mn, rows_dev, 1, nullptr, nullptr, parts, &P.proj, int64_t(P.Mn) * H, nullptr,
          handle->w.proj_norm, nullptr, nbuf, 0);
+    // every layer's K/V rows of W_qkv, up to kMaxGroups layers per launch
     const int64_t lstride = int64_t(P.kv.splits) * P.Mn * kvd;
-    for (int l = 0; l < c.num_layers; ++l) {
-      const dflash2_layer_weights& L = handle->layers[l];
-      const void* W = byte_offset(L.wqkv, int64_t(qd) * H * wb);
-      const float* sc = L.wqkv_scale ? L.wqkv_scale + qd : nullptr;
-      gemm(nbuf, H, W, dt == DFLASH2_FP8_E4M3 ? sc : nullptr, P.Mn, rows_dev, kvd, H, P.kv,
-           parts + l * lstride, normed);
+    for (int l0 = 0; l0 < c.num_layers; l0 += kMaxGroups) {
+      const int ng = std::min(kMaxGroups, c.num_layers - l0);
+      GemmArgs a{};
+      a.rs = normed;
+      a.X = nbuf; a.ldx = H; a.ldw = H;
+      a.P = parts + l0 * lstride; a.ldp = kvd; a.split_stride = int64_t(P.Mn) * kvd;
+      a.M = P.Mn; a.N = kvd; a.K = H; a.M_dev = rows_dev;
+      a.splits = P.kv.splits; a.k_split = P.kv.k_split;
+      a.groups = ng; a.group_stride = lstride;
+      for (int g = 0; g < ng; ++g) {
+        const dflash2_layer_weights& L = handle->layers[l0 + g];
+        a.Wg[g] = byte_offset(L.wqkv, int64_t(qd) * H * wb);
+        a.Sg[g] = (dt == DFLASH2_FP8_E4M3 && L.wqkv_scale) ? L.wqkv_scale + qd : nullptr;
+      }
+      a.W = a.Wg[0]; a.scale = a.Sg[0];
+      const int64_t bytes = ng * (int64_t(kvd) * H * wb + (a.Sg[0] ? int64_t(kvd) * 4 : 0) +
+                                  int64_t(P.Mn) * kvd * 4) + int64_t(P.Mn) * H * ab;
+      traced(stream, DFLASH2_K_GEMM, bytes, 2 * int64_t(ng) * P.Mn * kvd * H,
+             [&] { launch_gemm(dt, a, stream); });
     }
     KvAppendArgs ka{};
     ka.parts = parts; ka.splits = P.kv.splits; ka.split_stride = int64_t(P.Mn) * kvd; ka.ldp = kvd;
@@ -483,7 +496,7 @@ dflash2_status dflash2_select_path(dflash2_handle* handle, hipStream_t stream, i
     const int64_t bytes = int64_t(batch) * a.P * a.k * 8 + int64_t(batch) * (a.P * a.k + 1) * 2 * a.r * 4 +
                           int64_t(batch) * a.P * 8;
     traced(stream, DFLASH2_K_SELECT, bytes, 2 * pairs * a.r,
-           [&] { launch_select(a, select_lds(a.k, a.r, a.P), stream); });
+           [&] { launch_select(a, select_window(a.k, a.r, a.P, kSelectLds), stream); });
   }
   dflash2_status st = check_launch("select_path");
   return st == DFLASH2_OK ? ok() : st;

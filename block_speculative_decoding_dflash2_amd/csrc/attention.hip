@@ -232,8 +232,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs p) {
 }
 
 // One wave per (sequence, block row, q head): merge the chunk partials.
-// Lanes load the chunks' (max, sum) in parallel; the output sums run over
-// chunks in increasing order with the weights broadcast from their lanes.
+// Lanes load the chunks' (max, sum) in parallel.  For the output, lane
+// (cs, q) owns the 4 dimensions [4q, 4q + 4) and the chunks c = cs, cs + CS,
+// ... (CS = 64 / (d / 4) chunk subsets); the subsets are then added with
+// shuffles in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnCombineArgs p) {
   const int idx = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
@@ -249,39 +251,53 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnCombineArgs p) {
   const int CH = p.chunk_keys;
   const int nvalid = (L < 0 || n_end <= lo_al) ? 0 : min(p.nchunks, (n_end - lo_al + CH - 1) / CH);
   const int64_t cbase = (int64_t(b) * p.nkv + g) * p.nchunks;
+  const f32x2* ml = reinterpret_cast<const f32x2*>(p.part_ml);
   float M = -INFINITY;
-  for (int c = lane; c < nvalid; c += WAVE) M = fmaxf(M, p.part_ml[((cbase + c) * QS + s) * 2]);
+  for (int c = lane; c < nvalid; c += WAVE) M = fmaxf(M, ml[(cbase + c) * QS + s][0]);
   M = wave_max(M);
   float lsum = 0.f;
   for (int c = lane; c < nvalid; c += WAVE) {
-    const float mc = p.part_ml[((cbase + c) * QS + s) * 2];
-    if (mc != -INFINITY) lsum += p.part_ml[((cbase + c) * QS + s) * 2 + 1] * exp2_safe(mc - M);
+    const f32x2 v = ml[(cbase + c) * QS + s];
+    if (v[0] != -INFINITY) lsum += v[1] * exp2_safe(v[0] - M);
   }
   lsum = wave_sum(lsum);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  T* out = static_cast<T*>(p.o);
-  for (int d0 = 0; d0 < p.d; d0 += WAVE) {
-    const int dd = d0 + lane;
-    float acc = 0.f;
-    for (int cb = 0; cb < nvalid; cb += WAVE) {
-      float wgt = 0.f;
-      if (cb + lane < nvalid) {
-        const float mc = p.part_ml[((cbase + cb + lane) * QS + s) * 2];
-        wgt = mc != -INFINITY ? exp2_safe(mc - M) : 0.f;
-      }
-      const int n = min(WAVE, nvalid - cb);
-      const int ddc = dd < p.d ? dd : 0;
-      int c = 0;
-      for (; c + 8 <= n; c += 8) {    // eight loads in flight, summed in chunk order
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = p.part_o[((cbase + cb + c + u) * QS + s) * p.d + ddc];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc += v[u] * __shfl(wgt, c + u, WAVE);
-      }
-      for (; c < n; ++c) acc += p.part_o[((cbase + cb + c) * QS + s) * p.d + ddc] * __shfl(wgt, c, WAVE);
+
+  const int nq4 = p.d / 4;                  // 4 .. 64
+  const int CS = WAVE / nq4;                // chunk subsets
+  const int q = lane % nq4, cs = lane / nq4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < nvalid; cb += WAVE) {
+    float wgt = 0.f;
+    if (cb + lane < nvalid) {
+      const float mc = ml[(cbase + cb + lane) * QS + s][0];
+      wgt = mc != -INFINITY ? exp2_safe(mc - M) : 0.f;
     }
-    if (dd < p.d) Act<T>::store(out, (int64_t(b * p.bs + t) * p.nq + h) * p.d + dd, acc * inv);
+    const int n = min(WAVE, nvalid - cb);
+    for (int c0 = 0; c0 < n; c0 += 4 * CS) {  // same trip count on every lane
+      f32x4 v[4];
+      float w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + cs + u * CS;
+        const bool ok = c < n;
+        v[u] = *reinterpret_cast<const f32x4*>(p.part_o + ((cbase + cb + (ok ? c : 0)) * QS + s) * p.d + 4 * q);
+        const float wsrc = __shfl(wgt, ok ? c : 0, WAVE);
+        w[u] = ok ? wsrc : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += v[u] * w[u];
+    }
+  }
+  for (int off = nq4; off < WAVE; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off, WAVE);
+  }
+  if (cs == 0) {
+    T* out = static_cast<T*>(p.o);
+    const int64_t o = (int64_t(b * p.bs + t) * p.nq + h) * p.d + 4 * q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Act<T>::store(out, o + e, acc[e] * inv);
   }
 }
 

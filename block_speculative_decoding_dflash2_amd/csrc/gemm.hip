@@ -170,14 +170,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int n0 = (blockIdx.x * 4 + wave) * 16 * RT;
   const int m0 = blockIdx.y * 16 * RM;
   if (m0 >= Mact || n0 >= p.N) return;
-  const int kb = blockIdx.z * p.k_split;
+  const int split = blockIdx.z % p.splits, group = blockIdx.z / p.splits;
+  const void* Wp = p.groups > 1 ? p.Wg[group] : p.W;
+  const float* scale = p.groups > 1 ? p.Sg[group] : p.scale;
+  const int kb = split * p.k_split;
   const int ke = min(p.K, kb + p.k_split);
   f32x4 acc[RT][RM];
-  Tile::run(static_cast<const TA*>(p.X), p.ldx, static_cast<const TW*>(p.W), p.ldw, p.N, Mact, n0, m0,
+  Tile::run(static_cast<const TA*>(p.X), p.ldx, static_cast<const TW*>(Wp), p.ldw, p.N, Mact, n0, m0,
             kb, ke, acc, lds[wave]);
   const int lane = threadIdx.x & (WAVE - 1);
   const int r = lane & 15, g = lane >> 4;
-  float* P = p.P + int64_t(blockIdx.z) * p.split_stride;
+  float* P = p.P + int64_t(group) * p.group_stride + int64_t(split) * p.split_stride;
   float inv[RM];
 #pragma unroll
   for (int j = 0; j < RM; ++j) inv[j] = row_inv_rms(p.rs, min(m0 + 16 * j + r, Mact - 1));
@@ -185,9 +188,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   for (int i = 0; i < RT; ++i) {
     const int nb = n0 + 16 * i + 4 * g;
     float s[4] = {1.f, 1.f, 1.f, 1.f};
-    if (p.scale) {
+    if (scale) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] = p.scale[min(nb + e, p.N - 1)];
+      for (int e = 0; e < 4; ++e) s[e] = scale[min(nb + e, p.N - 1)];
     }
 #pragma unroll
     for (int j = 0; j < RM; ++j) {
@@ -283,34 +286,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 }
 
 // Final top-k over the per-group candidates of one row, then the logit
-// transform.  grid = (M), block = 256.  Candidates are staged in LDS when
-// they fit (use_lds); each round takes the largest key below the previous
-// one (keys are distinct because ids are).
-__global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p, int use_lds) {
-  extern __shared__ uint64_t cl[];
+// transform.  grid = (M), block = 256.  Keys are distinct (ids are), so the
+// k largest keys are the answer.  Each thread keeps a sorted list of its KMAX
+// best keys in registers (insertion network), the lists go to LDS, and k
+// rounds of a 256-way tournament over the list heads emit the result in
+// order.  k <= KMAX.
+template <int KMAX>
+__global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p) {
+  __shared__ uint64_t lists[256 * KMAX];
+  __shared__ uint64_t red[4];
+  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
+  const int m = blockIdx.x;
+  if (m >= Mact) return;
+  const int tid = threadIdx.x;
+  const uint64_t* c = p.cand + int64_t(m) * p.count;
+  uint64_t best[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) best[j] = 0ull;
+  for (int i0 = tid; i0 < p.count; i0 += 8 * 256) {
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256;
+      v[u] = i < p.count ? c[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      uint64_t x = v[u];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const uint64_t hi = best[j] > x ? best[j] : x;
+        x = best[j] > x ? x : best[j];
+        best[j] = hi;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) lists[tid * KMAX + j] = best[j];
+  __syncthreads();
+  int ptr = 0;
+  uint64_t head = lists[tid * KMAX];
+  for (int t = 0; t < p.k; ++t) {
+    uint64_t w = wave_max_u64(head);
+    if ((tid & (WAVE - 1)) == 0) red[tid / WAVE] = w;
+    __syncthreads();
+    w = red[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) w = red[q] > w ? red[q] : w;
+    __syncthreads();
+    if (head == w && w != 0ull) {  // the unique owner of the winning key advances
+      ++ptr;
+      head = ptr < KMAX ? lists[tid * KMAX + ptr] : 0ull;
+    }
+    if (tid == 0) {
+      float z = p.multiplier * key_val(w);
+      if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
+      p.ids[int64_t(m) * p.k + t] = int32_t(key_id(w));
+      p.vals[int64_t(m) * p.k + t] = z;
+    }
+  }
+}
+
+// The same result for k > 16: k rounds, each taking the largest key below the
+// previous one with a block-wide maximum over all candidates.
+__global__ __launch_bounds__(256) void topk_merge_rounds_kernel(TopkMergeArgs p) {
   __shared__ uint64_t red[4];
   const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
   const int m = blockIdx.x;
   if (m >= Mact) return;
   const uint64_t* c = p.cand + int64_t(m) * p.count;
-  if (use_lds) {
-    constexpr int U = 8;
-    for (int i0 = threadIdx.x; i0 < p.count; i0 += U * blockDim.x) {
-      uint64_t v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * blockDim.x;
-        v[u] = i < p.count ? c[i] : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * blockDim.x;
-        if (i < p.count) cl[i] = v[u];
-      }
-    }
-    __syncthreads();
-    c = cl;
-  }
   uint64_t prev = ~0ull;
   for (int t = 0; t < p.k; ++t) {
     uint64_t best = 0ull;
@@ -340,7 +384,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p, int us
 // ---------------------------------------------------------------------------
 template <typename TA, typename TW, int RT, int RM, int NSG>
 static void launch_gemm_t(const GemmArgs& a, hipStream_t s) {
-  dim3 grid((a.N + 64 * RT - 1) / (64 * RT), (a.M + 16 * RM - 1) / (16 * RM), a.splits);
+  dim3 grid((a.N + 64 * RT - 1) / (64 * RT), (a.M + 16 * RM - 1) / (16 * RM), a.splits * max(1, a.groups));
   hipLaunchKernelGGL((gemm_xwt_kernel<TA, TW, RT, RM, NSG>), grid, dim3(256), 0, s, a);
 }
 
@@ -378,9 +422,8 @@ void launch_lmhead_topk(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
 }
 
 void launch_topk_merge(const TopkMergeArgs& a, hipStream_t s) {
-  const size_t lds = size_t(a.count) * 8;
-  const int use_lds = lds <= 64 * 1024 ? 1 : 0;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(a.M), dim3(256), use_lds ? lds : 0, s, a, use_lds);
+  if (a.k <= 16) hipLaunchKernelGGL(topk_merge_kernel<16>, dim3(a.M), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(topk_merge_rounds_kernel, dim3(a.M), dim3(256), 0, s, a);
 }
 
 }  // namespace dfl

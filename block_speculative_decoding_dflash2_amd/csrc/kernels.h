@@ -6,6 +6,8 @@
 
 namespace dfl {
 
+constexpr int kMaxGroups = 8;
+
 // Per-row RMSNorm factor applied in a GEMM epilogue: row m is multiplied by
 // 1 / sqrt(sum_c sumsq[m][c] * inv_width + eps).  sumsq == null: factor 1.
 struct RowScale {
@@ -23,6 +25,12 @@ struct GemmArgs {
   const int32_t* M_dev;           // actual rows = min(*M_dev, M) if set
   int splits, k_split;            // K range per split (multiple of 32)
   RowScale rs;
+  // Grouped launch (groups > 1): group g multiplies weight Wg[g] (scale
+  // Sg[g]) and writes its partials at P + g * group_stride; grid z = splits * groups.
+  int groups;
+  const void* Wg[kMaxGroups];
+  const float* Sg[kMaxGroups];
+  int64_t group_stride;
 };
 
 struct LmHeadArgs {
@@ -138,7 +146,8 @@ int attn_sub_chunk(bool f32, int d);
 void launch_attention(bool f32, const AttnArgs& a, hipStream_t s);
 void launch_attn_combine(bool f32, const AttnCombineArgs& a, hipStream_t s);
 __host__ __device__ int select_row_stride(int r);
-void launch_select(const SelectArgs& a, size_t lds_bytes, hipStream_t s);
+int select_window(int k, int r, int P, size_t budget);
+void launch_select(const SelectArgs& a, int tw, hipStream_t s);
 void launch_verify_partial(const VerifyArgs& a, hipStream_t s);
 void launch_verify_final(const VerifyArgs& a, hipStream_t s);
 

@@ -14,6 +14,8 @@
 // "Prerequisites"): a row-wise argmax over the target logits, split into
 // chunks so the whole logit tensor streams through HBM once, then a tiny
 // kernel merges the chunks and finds the longest accepted prefix.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -56,62 +58,73 @@ __device__ __forceinline__ void pair_dot4(const float* __restrict__ a0, const fl
 
 __host__ __device__ int select_row_stride(int r) { return (r + 3) / 4 * 4 + 4; }
 
-// LDS layout: tl_rows [k][RS], tr_rows [k][RS], pair [k][k], S [k],
-// back [P][k] (int32).
-__global__ __launch_bounds__(64) void select_kernel(SelectArgs p) {
+// One block of 256 threads per sequence.  Pair scores depend only on the
+// candidate ids, so a window of `tw` transitions is done at once: the table
+// rows of its candidates are staged in LDS, all its pair scores are computed
+// in parallel, then wave 0 runs the max-sum recursion over the window (lane
+// j = candidate j; lanes of one wave run in lockstep, so S is read for every
+// i before any lane overwrites it).
+// LDS: TL [tw*k][RS], TR [tw*k][RS], PAIR [tw][k][k], S [k], BACK [P][k].
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int k = p.k, r = p.r, P = p.P, rs = select_row_stride(r);
   float* TL = lds;
-  float* TR = TL + k * rs;
-  float* PAIR = TR + k * rs;
-  float* S = PAIR + k * k;
+  float* TR = TL + tw * k * rs;
+  float* PAIR = TR + tw * k * rs;
+  float* S = PAIR + tw * k * k;
   int32_t* BACK = reinterpret_cast<int32_t*>(S + k);
   const int32_t* ids = p.ids + int64_t(b) * P * k;
   const float* vals = p.vals + int64_t(b) * P * k;
   const int V = p.V;
+  const int anchor = p.anchors[b];
 
-  // Rows of `table` for the n candidate ids (n <= 64): the ids are read once
-  // (one per lane) and shared through a shuffle; table loads go out eight at a time.
-  auto stage = [&](float* dst, const float* table, const int32_t* src_ids, int n) {
-    const int my_tok = lane < n ? src_ids[lane] : -1;
-    for (int idx0 = 0; idx0 < n * r; idx0 += 8 * WAVE) {
+  for (int t0 = 0; t0 < P; t0 += tw) {
+    const int nt = min(tw, P - t0);
+    // ---- stage: rows [0, nt*k) of TL and of TR, eight loads per thread in flight
+    const int nelem = 2 * nt * k * r;
+    for (int e0 = 0; e0 < nelem; e0 += 8 * 256) {
       float v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int idx = idx0 + u * WAVE + lane;
-        const int i = idx / r, m = idx - i * r;
-        const int tok = __shfl(my_tok, i < n ? i : 0, WAVE);
-        v[u] = (idx < n * r && tok >= 0 && tok < V) ? table[int64_t(tok) * r + m] : 0.f;
+        const int e = e0 + u * 256 + tid;
+        const int row = e / r, m = e - row * r;
+        const bool right = row >= nt * k;
+        const int rr = right ? row - nt * k : row;
+        const int w = rr / k, i = rr - w * k, t = t0 + w;
+        int tok = -1;
+        if (e < nelem) {
+          if (right) tok = ids[t * k + i];
+          else tok = t == 0 ? (i == 0 ? anchor : -1) : ids[(t - 1) * k + i];
+        }
+        const float* table = right ? p.tr : p.tl;
+        v[u] = (tok >= 0 && tok < V) ? table[int64_t(tok) * r + m] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int idx = idx0 + u * WAVE + lane;
-        const int i = idx / r, m = idx - i * r;
-        if (idx < n * r) dst[i * rs + m] = v[u];
+        const int e = e0 + u * 256 + tid;
+        const int row = e / r, m = e - row * r;
+        if (e < nelem) {
+          float* dst = row >= nt * k ? TR + (row - nt * k) * rs : TL + row * rs;
+          dst[m] = v[u];
+        }
       }
     }
-  };
-
-  for (int t = 0; t < P; ++t) {
-    // previous candidates: the anchor for t = 0
-    if (t == 0) stage(TL, p.tl, p.anchors + b, 1);
-    else stage(TL, p.tl, ids + (t - 1) * k, k);
-    stage(TR, p.tr, ids + t * k, k);
     __syncthreads();
-    const int nprev = t == 0 ? 1 : k;
-    const int npairs = nprev * k;
-    for (int q0 = lane; q0 < npairs; q0 += 4 * WAVE) {
+    // ---- pair scores of the window: PAIR[w][i][j] = pi(prev_i, cur_j)
+    const int npairs = nt * k * k;
+    for (int q0 = tid; q0 < npairs; q0 += 4 * 256) {
       int qi[4];
       const float* ap[4];
       const float* bp[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        qi[u] = q0 + u * WAVE;
+        qi[u] = q0 + u * 256;
         const int qq = qi[u] < npairs ? qi[u] : q0;
-        ap[u] = TL + (qq / k) * rs;
-        bp[u] = TR + (qq % k) * rs;
+        const int w = qq / (k * k), ij = qq - w * k * k, i = ij / k, j = ij - i * k;
+        ap[u] = TL + (w * k + i) * rs;
+        bp[u] = TR + (w * k + j) * rs;
       }
       float out[4];
       pair_dot4(ap[0], ap[1], ap[2], ap[3], bp[0], bp[1], bp[2], bp[3], r, out);
@@ -121,35 +134,43 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs p) {
     }
     __syncthreads();
     if (p.debug_pair) {
-      float* dp = p.debug_pair + (int64_t(b) * P + t) * k * k;
-      for (int idx = lane; idx < k * k; idx += WAVE) {
-        const int i = idx / k, j = idx % k;
-        dp[idx] = PAIR[(t == 0 ? 0 : i) * k + j];
+      for (int q = tid; q < npairs; q += 256) {
+        const int w = q / (k * k), ij = q - w * k * k, i = ij / k, j = ij - i * k;
+        const int t = t0 + w;
+        p.debug_pair[(int64_t(b) * P + t) * k * k + ij] = PAIR[w * k * k + (t == 0 ? 0 : i) * k + j];
       }
     }
-    float snew = 0.f;
-    int bi = 0;
-    if (lane < k) {
-      const int j = lane;
-      if (t == 0) {
-        snew = PAIR[j] + vals[j];
-      } else {
-        float bv = S[0] + PAIR[j];
-        for (int i = 1; i < k; ++i) {
-          const float v = S[i] + PAIR[i * k + j];
-          if (v > bv) { bv = v; bi = i; }
+    // ---- max-sum recursion over the window (wave 0)
+    if (tid < WAVE) {
+      for (int w = 0; w < nt; ++w) {
+        const int t = t0 + w;
+        const float* pr = PAIR + w * k * k;
+        float snew = 0.f;
+        int bi = 0;
+        if (tid < k) {
+          const int j = tid;
+          if (t == 0) {
+            snew = pr[j] + vals[j];
+          } else {
+            float bv = S[0] + pr[j];
+            for (int i = 1; i < k; ++i) {
+              const float v = S[i] + pr[i * k + j];
+              if (v > bv) { bv = v; bi = i; }
+            }
+            snew = bv + vals[t * k + j];
+          }
         }
-        snew = bv + vals[t * k + j];
+        __builtin_amdgcn_wave_barrier();
+        if (tid < k) {
+          S[tid] = snew;
+          BACK[t * k + tid] = bi;
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-    }
-    __syncthreads();
-    if (lane < k) {
-      S[lane] = snew;
-      BACK[t * k + lane] = bi;
     }
     __syncthreads();
   }
-  if (lane == 0) {
+  if (tid == 0) {
     int j = 0;
     float best = S[0];
     for (int i = 1; i < k; ++i)
@@ -163,8 +184,20 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs p) {
   }
 }
 
-void launch_select(const SelectArgs& a, size_t lds_bytes, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(64), lds_bytes, s, a);
+// Transitions per window that fit the LDS budget (0: does not fit).
+int select_window(int k, int r, int P, size_t budget) {
+  const size_t per = size_t(2 * k * select_row_stride(r) + k * k) * 4;
+  const size_t fixed = size_t(k + P * k) * 4;
+  if (fixed + per > budget) return 0;
+  return int(std::min<size_t>(size_t(P), (budget - fixed) / per));
+}
+
+static size_t select_lds_bytes(int k, int r, int P, int tw) {
+  return size_t(2 * tw * k * select_row_stride(r) + tw * k * k + k + P * k) * 4;
+}
+
+void launch_select(const SelectArgs& a, int tw, hipStream_t s) {
+  hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(256), select_lds_bytes(a.k, a.r, a.P, tw), s, a, tw);
 }
 
 // grid = (nchunks, B * bs), block = 256: best (value, id) key of one chunk.
