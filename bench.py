@@ -32,6 +32,33 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources; a traffic measurement is only used
+    while the kernels are unchanged since it was taken."""
+    import hashlib
+    csrc = os.path.join(ROOT, "block_speculative_decoding_dflash2_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by the counter's reading
+    for a 1 GiB copy), or None if absent or taken on other kernel sources."""
+    import json
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -40,6 +67,8 @@ def main():
     ap.add_argument("--workload", default="dense27b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the step shards by sequence with no exchange, so "
@@ -91,6 +120,14 @@ def main():
                           want_score=False)
         verify_accept(drafts, target, workspace=vws, accepted=accepted, bonus=bonus)
 
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 1 GiB read + 1 GiB written")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -137,6 +174,7 @@ def main():
                          "avg_launch_us": round(d["ms"] * 1e3 / d["launches"], 2),
                          "bytes_per_launch": d["bytes"] // d["launches"],
                          "share_of_kernel_time": round(d["ms"] / traced_total, 3)})
+        roofline["traffic"] = measured_traffic(w.name, dom)
         for kind, dd in sorted(per_kind.items(), key=lambda kv: -kv[1]["ms"]):
             log(f"  {kind:15s} {dd['launches'] // args.steps:3d}/step {dd['ms'] * 1e3 / args.steps:9.1f} us/step "
                 f"{dd['bytes'] / max(dd['ms'], 1e-9) / 1e6:8.1f} GB/s")
@@ -150,12 +188,19 @@ def main():
         import oracle as O
         from threadpoolctl import threadpool_info
         nthreads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        t1 = time.time()
-        O.step(w, W, inp)
-        dt = time.time() - t1
+        # whole oracle steps of the same workload, repeated until ~10 s of CPU
+        # work (at most 30 s); throughput = blocks / mean step time
+        t_all, reps = 0.0, 0
+        while reps < 1 or (t_all < 10.0 and t_all + t_all / reps < 30.0):
+            t1 = time.time()
+            O.step(w, W, inp)
+            t_all += time.time() - t1
+            reps += 1
+        dt = t_all / reps
         cpu = {"value": round(B / dt, 6), "unit": "blocks/s", "cores": int(nthreads), "kind": "oracle",
-               "sample": f"one full step of {w.name} ({B} block(s)); float64 NumPy oracle, {dt:.1f}s"}
-        log(f"oracle step {dt:.1f}s with {nthreads} BLAS threads")
+               "sample": f"{reps} full steps of {w.name} ({B} block(s) each), float64 NumPy oracle, "
+                         f"{t_all:.1f}s in total"}
+        log(f"oracle: {reps} steps, {dt:.2f}s each, {nthreads} BLAS threads")
 
     out = {
         "metric": "drafted blocks/s per MI355X",
