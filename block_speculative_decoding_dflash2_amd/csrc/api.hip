@@ -54,10 +54,10 @@ void traced(hipStream_t s, int kind, int64_t bytes, int64_t flops, F&& launch) {
     e->kind = kind;
     e->bytes = bytes;
     e->flops = flops;
-    hipEventRecord(e->start, s);
+    (void)hipEventRecord(e->start, s);
   }
   launch();
-  if (e) hipEventRecord(e->stop, s);
+  if (e) (void)hipEventRecord(e->stop, s);
 }
 
 // Plans are a pure function of the shapes (not of the device), so results

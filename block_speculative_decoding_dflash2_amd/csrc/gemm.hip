@@ -286,63 +286,81 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 }
 
 // Final top-k over the per-group candidates of one row, then the logit
-// transform.  grid = (M), block = 256.  Keys are distinct (ids are), so the
-// k largest keys are the answer.  Each thread keeps a sorted list of its KMAX
-// best keys in registers (insertion network), the lists go to LDS, and k
-// rounds of a 256-way tournament over the list heads emit the result in
-// order.  k <= KMAX.
+// transform.  grid = (M), block = 256.  The lm_head kernel emits each vocab
+// group's k candidates sorted (largest key first) and keys are distinct
+// (ids are).  Each thread folds whole groups into a sorted list of KMAX keys;
+// two sorted lists combine into the KMAX largest of their union by taking
+// max(a[i], b[KMAX-1-i]) (a bitonic sequence) and sorting that with a
+// bitonic half-cleaner cascade.  Lists are combined across lanes by xor
+// shuffles, then across the four waves through LDS.  k <= KMAX.
 template <int KMAX>
-__global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p) {
-  __shared__ uint64_t lists[256 * KMAX];
-  __shared__ uint64_t red[4];
-  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
-  const int m = blockIdx.x;
-  if (m >= Mact) return;
-  const int tid = threadIdx.x;
-  const uint64_t* c = p.cand + int64_t(m) * p.count;
-  uint64_t best[KMAX];
+__device__ __forceinline__ void bitonic_top(uint64_t (&a)[KMAX], const uint64_t (&brev)[KMAX]) {
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) best[j] = 0ull;
-  for (int i0 = tid; i0 < p.count; i0 += 8 * 256) {
-    uint64_t v[8];
+  for (int i = 0; i < KMAX; ++i) a[i] = a[i] > brev[i] ? a[i] : brev[i];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * 256;
-      v[u] = i < p.count ? c[i] : 0ull;
-    }
+  for (int half = KMAX / 2; half >= 1; half >>= 1) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      uint64_t x = v[u];
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        const uint64_t hi = best[j] > x ? best[j] : x;
-        x = best[j] > x ? x : best[j];
-        best[j] = hi;
+    for (int i = 0; i < KMAX; ++i) {
+      if ((i & half) == 0) {
+        const uint64_t x = a[i], y = a[i + half];
+        a[i] = x > y ? x : y;
+        a[i + half] = x > y ? y : x;
       }
     }
   }
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p) {
+  __shared__ uint64_t lists[4 * KMAX];
+  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
+  const int m = blockIdx.x;
+  if (m >= Mact) return;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const uint64_t* c = p.cand + int64_t(m) * p.count;
+  const int groups = p.count / p.k;
+  uint64_t best[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) lists[tid * KMAX + j] = best[j];
-  __syncthreads();
-  int ptr = 0;
-  uint64_t head = lists[tid * KMAX];
-  for (int t = 0; t < p.k; ++t) {
-    uint64_t w = wave_max_u64(head);
-    if ((tid & (WAVE - 1)) == 0) red[tid / WAVE] = w;
-    __syncthreads();
-    w = red[0];
+  for (int j = 0; j < KMAX; ++j) best[j] = 0ull;
+  for (int gi = tid; gi < groups; gi += 256) {
+    uint64_t brev[KMAX];
 #pragma unroll
-    for (int q = 1; q < 4; ++q) w = red[q] > w ? red[q] : w;
-    __syncthreads();
-    if (head == w && w != 0ull) {  // the unique owner of the winning key advances
-      ++ptr;
-      head = ptr < KMAX ? lists[tid * KMAX + ptr] : 0ull;
+    for (int j = 0; j < KMAX; ++j) {
+      const int src = KMAX - 1 - j;                 // reversed: ascending
+      brev[j] = src < p.k ? c[int64_t(gi) * p.k + src] : 0ull;
     }
-    if (tid == 0) {
-      float z = p.multiplier * key_val(w);
-      if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
-      p.ids[int64_t(m) * p.k + t] = int32_t(key_id(w));
-      p.vals[int64_t(m) * p.k + t] = z;
+    bitonic_top<KMAX>(best, brev);
+  }
+  for (int d = 1; d < WAVE; d <<= 1) {
+    uint64_t brev[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) brev[j] = __shfl_xor(best[KMAX - 1 - j], d, WAVE);
+    bitonic_top<KMAX>(best, brev);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) lists[wave * KMAX + j] = best[j];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) best[j] = lane < 4 ? lists[lane * KMAX + j] : 0ull;
+    for (int d = 1; d < 4; d <<= 1) {
+      uint64_t brev[KMAX];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) brev[j] = __shfl_xor(best[KMAX - 1 - j], d, WAVE);
+      bitonic_top<KMAX>(best, brev);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < KMAX; ++t) {
+        if (t < p.k) {
+          float z = p.multiplier * key_val(best[t]);
+          if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
+          p.ids[int64_t(m) * p.k + t] = int32_t(key_id(best[t]));
+          p.vals[int64_t(m) * p.k + t] = z;
+        }
+      }
     }
   }
 }

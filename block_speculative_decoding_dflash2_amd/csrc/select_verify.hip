@@ -64,7 +64,8 @@ __host__ __device__ int select_row_stride(int r) { return (r + 3) / 4 * 4 + 4; }
 // in parallel, then wave 0 runs the max-sum recursion over the window (lane
 // j = candidate j; lanes of one wave run in lockstep, so S is read for every
 // i before any lane overwrites it).
-// LDS: TL [tw*k][RS], TR [tw*k][RS], PAIR [tw][k][k], S [k], BACK [P][k].
+// LDS: TL [tw*k][RS], TR [tw*k][RS], PAIR [tw][k][k], S [k], BACK [P][k],
+// PATH [P], TOK [2*tw*k], VAL [tw*k].
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int b = blockIdx.x;
@@ -75,6 +76,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
   float* PAIR = TR + tw * k * rs;
   float* S = PAIR + tw * k * k;
   int32_t* BACK = reinterpret_cast<int32_t*>(S + k);
+  int32_t* PATH = BACK + p.P * p.k;
+  int32_t* TOK = PATH + p.P;
+  float* VAL = reinterpret_cast<float*>(TOK + 2 * tw * p.k);
+  const bool vec4 = (r & 3) == 0 &&
+                    ((reinterpret_cast<uintptr_t>(p.tl) | reinterpret_cast<uintptr_t>(p.tr)) & 15) == 0;
   const int32_t* ids = p.ids + int64_t(b) * P * k;
   const float* vals = p.vals + int64_t(b) * P * k;
   const int V = p.V;
@@ -82,32 +88,65 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
 
   for (int t0 = 0; t0 < P; t0 += tw) {
     const int nt = min(tw, P - t0);
-    // ---- stage: rows [0, nt*k) of TL and of TR, eight loads per thread in flight
-    const int nelem = 2 * nt * k * r;
-    for (int e0 = 0; e0 < nelem; e0 += 8 * 256) {
-      float v[8];
+    // ---- stage: the window's candidate ids (left rows: the previous
+    // position's candidates, the anchor alone at t = 0; right rows: the
+    // current position's), then their table rows, all loads of a thread
+    // issued before any is used
+    const int nrows = 2 * nt * k;
+    for (int q = tid; q < nrows; q += 256) {
+      const bool right = q >= nt * k;
+      const int rr = right ? q - nt * k : q;
+      const int w = rr / k, i = rr - w * k, t = t0 + w;
+      int tok;
+      if (right) tok = ids[t * k + i];
+      else tok = t == 0 ? (i == 0 ? anchor : -1) : ids[(t - 1) * k + i];
+      TOK[q] = (tok >= 0 && tok < V) ? tok : -1;
+    }
+    for (int q = tid; q < nt * k; q += 256) VAL[q] = vals[t0 * k + q];
+    __syncthreads();
+    if (vec4) {
+      const int nv = r >> 2, total = nrows * nv;
+      for (int e0 = 0; e0 < total; e0 += 16 * 256) {
+        f32x4 v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * 256 + tid;
-        const int row = e / r, m = e - row * r;
-        const bool right = row >= nt * k;
-        const int rr = right ? row - nt * k : row;
-        const int w = rr / k, i = rr - w * k, t = t0 + w;
-        int tok = -1;
-        if (e < nelem) {
-          if (right) tok = ids[t * k + i];
-          else tok = t == 0 ? (i == 0 ? anchor : -1) : ids[(t - 1) * k + i];
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + u * 256 + tid;
+          const int row = e / nv, mv = e - row * nv;
+          const int tok = e < total ? TOK[row] : -1;
+          const float* table = row >= nt * k ? p.tr : p.tl;
+          v[u] = tok >= 0 ? *reinterpret_cast<const f32x4*>(table + int64_t(tok) * r + 4 * mv)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        const float* table = right ? p.tr : p.tl;
-        v[u] = (tok >= 0 && tok < V) ? table[int64_t(tok) * r + m] : 0.f;
-      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * 256 + tid;
-        const int row = e / r, m = e - row * r;
-        if (e < nelem) {
-          float* dst = row >= nt * k ? TR + (row - nt * k) * rs : TL + row * rs;
-          dst[m] = v[u];
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + u * 256 + tid;
+          const int row = e / nv, mv = e - row * nv;
+          if (e < total) {
+            float* dst = row >= nt * k ? TR + (row - nt * k) * rs : TL + row * rs;
+            *reinterpret_cast<f32x4*>(dst + 4 * mv) = v[u];
+          }
+        }
+      }
+    } else {
+      const int total = nrows * r;
+      for (int e0 = 0; e0 < total; e0 += 8 * 256) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * 256 + tid;
+          const int row = e / r, m = e - row * r;
+          const int tok = e < total ? TOK[row] : -1;
+          const float* table = row >= nt * k ? p.tr : p.tl;
+          v[u] = tok >= 0 ? table[int64_t(tok) * r + m] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * 256 + tid;
+          const int row = e / r, m = e - row * r;
+          if (e < total) {
+            float* dst = row >= nt * k ? TR + (row - nt * k) * rs : TL + row * rs;
+            dst[m] = v[u];
+          }
         }
       }
     }
@@ -150,14 +189,26 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
         if (tid < k) {
           const int j = tid;
           if (t == 0) {
-            snew = pr[j] + vals[j];
+            snew = pr[j] + VAL[j];
           } else {
-            float bv = S[0] + pr[j];
-            for (int i = 1; i < k; ++i) {
-              const float v = S[i] + pr[i * k + j];
-              if (v > bv) { bv = v; bi = i; }
+            float bv = 0.f;
+            for (int i0 = 0; i0 < k; i0 += 8) {
+              float sv[8], pv[8];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u;
+                sv[u] = i < k ? S[i] : 0.f;
+                pv[u] = i < k ? pr[i * k + j] : 0.f;
+              }
+#pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u;
+                const float v = sv[u] + pv[u];
+                if (i == 0) bv = v;
+                else if (i < k && v > bv) { bv = v; bi = i; }
+              }
             }
-            snew = bv + vals[t * k + j];
+            snew = bv + VAL[w * k + j];
           }
         }
         __builtin_amdgcn_wave_barrier();
@@ -170,6 +221,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
     }
     __syncthreads();
   }
+  // ---- trace back through LDS, then write the path and its tokens in parallel
   if (tid == 0) {
     int j = 0;
     float best = S[0];
@@ -177,23 +229,28 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
       if (S[i] > best) { best = S[i]; j = i; }
     if (p.score) p.score[b] = best;
     for (int t = P - 1; t >= 0; --t) {
-      p.path[int64_t(b) * P + t] = j;
-      p.drafts[int64_t(b) * P + t] = ids[t * k + j];
+      PATH[t] = j;
       j = BACK[t * k + j];
     }
+  }
+  __syncthreads();
+  for (int t = tid; t < P; t += 256) {
+    const int j = PATH[t];
+    p.path[int64_t(b) * P + t] = j;
+    p.drafts[int64_t(b) * P + t] = ids[t * k + j];
   }
 }
 
 // Transitions per window that fit the LDS budget (0: does not fit).
 int select_window(int k, int r, int P, size_t budget) {
-  const size_t per = size_t(2 * k * select_row_stride(r) + k * k) * 4;
-  const size_t fixed = size_t(k + P * k) * 4;
+  const size_t per = size_t(2 * k * select_row_stride(r) + k * k + 3 * k) * 4;
+  const size_t fixed = size_t(k + P * k + P) * 4;
   if (fixed + per > budget) return 0;
   return int(std::min<size_t>(size_t(P), (budget - fixed) / per));
 }
 
 static size_t select_lds_bytes(int k, int r, int P, int tw) {
-  return size_t(2 * tw * k * select_row_stride(r) + tw * k * k + k + P * k) * 4;
+  return size_t(2 * tw * k * select_row_stride(r) + tw * k * k + k + P * k + P + 3 * tw * k) * 4;
 }
 
 void launch_select(const SelectArgs& a, int tw, hipStream_t s) {
