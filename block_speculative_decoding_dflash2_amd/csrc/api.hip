@@ -77,10 +77,32 @@ struct Split {
   int splits = 1, k_split = 0;
 };
 
-Split plan_split(int dtype, int M, int N, int K) {
+constexpr int kCUs = 256;
+
+Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
   Split s;
+  if (gemm_tiled_ok(dtype, M, K)) {
+    // compute-bound tiles: pick the split count with the shortest makespan,
+    // counting waves of one tile per CU, each costing its k range plus a
+    // fixed epilogue/prologue cost of about 512 k; ties go to fewer splits
+    const int64_t tiles = cdiv(M, tiled_block_rows(M)) * cdiv(N, 256) * groups;
+    int best = 1;
+    double best_cost = 1e300;
+    for (int S = 1; S <= 16; ++S) {
+      const int64_t ks = cdiv(cdiv(K, S), 64) * 64;
+      if (cdiv(K, ks) != S) continue;
+      const double cost = double(cdiv(tiles * S, kCUs)) * double(ks + 512);
+      if (cost < best_cost * 0.97) {
+        best_cost = cost;
+        best = S;
+      }
+    }
+    s.k_split = int(cdiv(cdiv(K, best), 64) * 64);
+    s.splits = int(cdiv(K, s.k_split));
+    return s;
+  }
   const int mtile = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
-  const int64_t blocks = cdiv(N, gemm_rows_per_block(dtype, M)) * cdiv(M, mtile);
+  const int64_t blocks = cdiv(N, gemm_rows_per_block(dtype, M)) * cdiv(M, mtile) * groups;
   int S = 1;
   if (M <= 64) {
     S = int(cdiv(kTargetBlocks, blocks));
@@ -132,7 +154,7 @@ Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
   const int H = c.hidden, qd = c.num_q_heads * c.head_dim, kvd = 2 * c.num_kv_heads * c.head_dim;
   const int qkvd = qd + kvd, F = c.ffn, dt = c.weight_dtype;
   p.proj = plan_split(dt, std::max(p.Mn, 1), H, c.num_taps * c.tap_width);
-  p.kv = plan_split(dt, std::max(p.Mn, 1), kvd, H);
+  p.kv = plan_split(dt, std::max(p.Mn, 1), kvd, H, std::min(c.num_layers, kMaxGroups));
   p.qkv = plan_split(dt, p.M, qkvd, H);
   p.o = plan_split(dt, p.M, H, qd);
   p.gu = plan_split(dt, p.M, 2 * F, H);

@@ -423,6 +423,10 @@ int gemm_rows_per_block(int weight_dtype, int M) {
 }
 
 void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s) {
+  if (gemm_tiled_ok(weight_dtype, a.M, a.K)) {
+    launch_gemm_tiled(weight_dtype, a, s);
+    return;
+  }
   switch (weight_dtype) {
     case 0: launch_gemm_rm<float, float>(a, s); break;
     case 1: launch_gemm_rm<bf16_t, bf16_t>(a, s); break;
@@ -431,6 +435,10 @@ void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s) {
 }
 
 void launch_lmhead_topk(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
+  if (lmhead_tiled_ok(weight_dtype, a.M, a.K, a.k)) {
+    launch_lmhead_tiled(weight_dtype, a, s);
+    return;
+  }
   dim3 grid(a.groups, (a.M + 15) / 16);
   switch (weight_dtype) {
     case 0: hipLaunchKernelGGL((lmhead_topk_kernel<float, float>), grid, dim3(256), 0, s, a); break;

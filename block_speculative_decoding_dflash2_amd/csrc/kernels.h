@@ -132,7 +132,15 @@ struct VerifyArgs {
   int32_t* accepted; int32_t* bonus; int32_t* argmax;
 };
 
+// Activation rows above which the LDS-tiled, compute-bound GEMMs are used.
+constexpr int kTiledMinRows = 64;
+
 int gemm_rows_per_block(int weight_dtype, int M);
+bool gemm_tiled_ok(int weight_dtype, int M, int K);
+bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k);
+int tiled_block_rows(int M);
+void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s);
+void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s);
 void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s);
 void launch_lmhead_topk(int weight_dtype, const LmHeadArgs& a, hipStream_t s);
 void launch_topk_merge(const TopkMergeArgs& a, hipStream_t s);

@@ -168,7 +168,13 @@ SMALL_FP8 = SMALL_BF16.replace(name="small_fp8", index=11, weight_dtype="fp8", b
 SMALL_FP32 = SMALL_BF16.replace(name="small_fp32", index=12, weight_dtype="fp32", batch=2,
                                 block_size=5, cold=True, ctx=(70, 70), vocab=1000)
 
-TEST_WORKLOADS = {w.name: w for w in (SMALL_BF16, SMALL_FP8, SMALL_FP32)}
+# Many activation rows (the compute-bound, LDS-tiled GEMM path) at small
+# widths: ragged row tiles, a ragged vocabulary tile, and (fp8) two row tiles.
+MEDIUM_BF16 = SMALL_BF16.replace(name="medium_bf16", index=13, batch=24, ffn=768, vocab=3001)
+MEDIUM_FP8 = SMALL_BF16.replace(name="medium_fp8", index=14, weight_dtype="fp8", batch=40,
+                                block_size=7, ffn=768, top_k=8, vocab=2500, ctx=(40, 200))
+
+TEST_WORKLOADS = {w.name: w for w in (SMALL_BF16, SMALL_FP8, SMALL_FP32, MEDIUM_BF16, MEDIUM_FP8)}
 
 
 def get(name: str) -> Workload:

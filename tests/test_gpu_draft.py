@@ -107,7 +107,8 @@ def check_step(g: DraftRun, res, seqs):
     assert np.array_equal(got["bonus"].cpu().numpy()[same], want["bonus"][same])
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "small_fp32", "small_bf16", "small_fp8"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "small_fp32", "small_bf16", "small_fp8", "medium_bf16",
+                                  "medium_fp8"])
 def test_draft_small_workloads(name):
     w = synth.get(name)
     g = DraftRun(w)
