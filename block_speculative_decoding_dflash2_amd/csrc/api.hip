@@ -189,7 +189,9 @@ Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
   const size_t attn_rows = size_t(B) * c.num_kv_heads * p.attn.nchunks * p.attn.qs;
   p.off_attn_o = take(attn_rows * c.head_dim * 4);
   p.off_attn_ml = take(attn_rows * 2 * 4);
-  p.off_cand = take(size_t(p.Mh) * p.groups * c.selector_top_k * 8);
+  // candidate lists: the weight-streaming lm_head writes groups x k keys per
+  // row, the tiled one at most groups lists of 16
+  p.off_cand = take(size_t(p.Mh) * p.groups * std::max(c.selector_top_k, 16) * 8);
   p.total = off;
   return p;
 }
@@ -489,7 +491,14 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
            [&] { launch_lmhead_topk(dt, la, stream); });
   }
   TopkMergeArgs ma{};
-  ma.cand = la.cand; ma.count = P.groups * c.selector_top_k; ma.M = P.Mh; ma.k = c.selector_top_k;
+  ma.cand = la.cand; ma.M = P.Mh; ma.k = c.selector_top_k;
+  if (lmhead_tiled_ok(dt, P.Mh, H, c.selector_top_k)) {
+    ma.glen = 16;
+    ma.count = lmhead_tiled_lists(P.Mh, c.vocab) * 16;
+  } else {
+    ma.glen = c.selector_top_k;
+    ma.count = P.groups * c.selector_top_k;
+  }
   ma.M_dev = nullptr; ma.ids = topk_ids; ma.vals = topk_vals;
   ma.multiplier = c.output_multiplier; ma.softcap = c.final_logit_softcapping;
   traced(stream, DFLASH2_K_TOPK_MERGE, int64_t(P.Mh) * ma.count * 8 + int64_t(P.Mh) * ma.k * 8, 0,

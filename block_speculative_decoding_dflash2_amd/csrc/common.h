@@ -97,12 +97,18 @@ template <> struct WFrag<bf16_t> {
   typedef Frag8Bf16 frag;
   typedef u32x4 raw;
   __device__ static raw load(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+  __device__ static raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  }
   __device__ static void cvt(frag& f, raw r) { f.v = __builtin_bit_cast(bf16x8, r); }
 };
 template <> struct WFrag<fp8_t> {
   typedef Frag8Bf16 frag;
   typedef u32x2 raw;
   __device__ static raw load(const fp8_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+  __device__ static raw load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  }
   __device__ static void cvt(frag& f, raw r) { fp8x8_to_frag(f, r); }
 };
 struct RawF32x8 { f32x4 a, b; };
@@ -175,6 +181,27 @@ __device__ __forceinline__ uint64_t rank_key(float v, uint32_t id) {
   return (uint64_t(ordered_f32(v)) << 32) | uint64_t(0xFFFFFFFFu - id);
 }
 __device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - uint32_t(k); }
+
+// a (KMAX keys, largest first) <- the KMAX largest keys of a and b, largest
+// first, where brev holds b smallest first: max(a[i], brev[i]) is a bitonic
+// sequence holding them, sorted by a half-cleaner cascade.
+template <int KMAX>
+__device__ __forceinline__ void bitonic_top(uint64_t (&a)[KMAX], const uint64_t (&brev)[KMAX]) {
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) a[i] = a[i] > brev[i] ? a[i] : brev[i];
+#pragma unroll
+  for (int half = KMAX / 2; half >= 1; half >>= 1) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if ((i & half) == 0) {
+        const uint64_t x = a[i], y = a[i + half];
+        a[i] = x > y ? x : y;
+        a[i + half] = x > y ? y : x;
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ float key_val(uint64_t k) { return unordered_f32(uint32_t(k >> 32)); }
 
 }  // namespace dfl

@@ -286,30 +286,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 }
 
 // Final top-k over the per-group candidates of one row, then the logit
-// transform.  grid = (M), block = 256.  The lm_head kernel emits each vocab
-// group's k candidates sorted (largest key first) and keys are distinct
+// transform.  grid = (M), block = 256.  The lm_head kernels emit sorted
+// lists of glen keys (largest first; glen <= KMAX) and keys are distinct
 // (ids are).  Each thread folds whole groups into a sorted list of KMAX keys;
 // two sorted lists combine into the KMAX largest of their union by taking
 // max(a[i], b[KMAX-1-i]) (a bitonic sequence) and sorting that with a
 // bitonic half-cleaner cascade.  Lists are combined across lanes by xor
 // shuffles, then across the four waves through LDS.  k <= KMAX.
-template <int KMAX>
-__device__ __forceinline__ void bitonic_top(uint64_t (&a)[KMAX], const uint64_t (&brev)[KMAX]) {
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) a[i] = a[i] > brev[i] ? a[i] : brev[i];
-#pragma unroll
-  for (int half = KMAX / 2; half >= 1; half >>= 1) {
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      if ((i & half) == 0) {
-        const uint64_t x = a[i], y = a[i + half];
-        a[i] = x > y ? x : y;
-        a[i + half] = x > y ? y : x;
-      }
-    }
-  }
-}
-
 template <int KMAX>
 __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p) {
   __shared__ uint64_t lists[4 * KMAX];
@@ -318,7 +301,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p) {
   if (m >= Mact) return;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const uint64_t* c = p.cand + int64_t(m) * p.count;
-  const int groups = p.count / p.k;
+  const int groups = p.count / p.glen;
   uint64_t best[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) best[j] = 0ull;
@@ -327,7 +310,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkMergeArgs p) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const int src = KMAX - 1 - j;                 // reversed: ascending
-      brev[j] = src < p.k ? c[int64_t(gi) * p.k + src] : 0ull;
+      brev[j] = src < p.glen ? c[int64_t(gi) * p.glen + src] : 0ull;
     }
     bitonic_top<KMAX>(best, brev);
   }

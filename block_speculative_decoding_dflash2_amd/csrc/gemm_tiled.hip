@@ -3,15 +3,16 @@
 // where every weight row meets hundreds of activation rows and the matrix
 // cores, not HBM, set the pace.
 //
-// Block tile: BM = 16 * FM activation rows x 256 weight rows, 4 waves; wave w
+// Block tile: BM = 128 activation rows x 256 weight rows, 4 waves; wave w
 // owns weight rows [64 w, 64 w + 64) of the tile against all BM activation
-// rows (acc = 2 x BM/32 MFMA 32x32x16 tiles, BM/2 float32 per lane).  The
-// activation tile is shared by the four waves and goes through LDS (double
-// buffered, 64 k per stage, rows padded to 144 bytes so 16-byte reads are
-// conflict-free).  Weight fragments are private to a wave, so they are read
-// straight from global memory into MFMA operand registers (one stage ahead)
-// and never touch LDS, which halves LDS traffic against staging both
-// operands.  fp8 weights are widened to bf16 in registers (exact).
+// rows (acc = 2 x 4 MFMA 32x32x16 tiles, 64 float32 per lane), and two
+// blocks share a CU.  The activation tile is shared by the four waves and
+// goes through LDS (double buffered, 64 k per stage, rows padded to 144 bytes
+// so 16-byte reads are conflict-free).  Weight rows are private to a wave:
+// each wave fetches its 64 rows with coalesced loads one stage ahead into
+// registers and copies them into its own LDS region, from which they are
+// read in MFMA operand order.  fp8 weights are widened to bf16 when read
+// from LDS (exact).
 //
 // Tiles are numbered with the activation tile fastest and dealt out so that
 // each XCD (blocks go to the 8 XCDs round-robin) runs a contiguous run of
@@ -30,6 +31,8 @@ constexpr int kTBN = 256;            // weight rows per block (64 per wave)
 constexpr int kTKT = 64;             // contraction depth per LDS stage
 constexpr int kTXRow = kTKT * 2 + 16;  // LDS bytes per activation row
 constexpr int kTSlots = 32;          // top-k candidate slots per row and round
+// Buffer resource word 3 for untyped 32-bit data on gfx9-family chips.
+constexpr int kBufferFlags = 0x00020000;
 }  // namespace
 
 struct TiledArgs {
@@ -47,9 +50,27 @@ struct TiledArgs {
   float* P; int64_t ldp, split_stride;       // partial-sum epilogue
   int k, vgroups; uint64_t* cand; float* debug_logits;  // top-k epilogue
   int nM, nN, tiles;
+  int tpb;                                    // vocabulary tiles per lm_head block
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Weight rows go through a wave-private LDS region: they are fetched with
+// coalesced 16-byte loads (whole 128-byte row segments, 8 lanes per row for
+// bf16) and read back in MFMA operand order.  Fetching them straight in
+// operand order (32 rows x 32 bytes per instruction) runs at about a quarter
+// of the L2 rate on this chip and starves the matrix cores.
+template <typename TW> struct WLds;
+template <> struct WLds<bf16_t> {
+  static constexpr int ROWB = 144;   // 128 B of a stage + pad
+  static constexpr int NLD = 8;      // coalesced 16-byte loads per lane per stage (8 rows x 128 B each)
+  typedef u32x4 raw;
+};
+template <> struct WLds<fp8_t> {
+  static constexpr int ROWB = 80;
+  static constexpr int NLD = 4;      // 16 rows x 64 B each
+  typedef u32x4 raw;
+};
 
 // Main loop on v_mfma_f32_32x32x16_bf16: D[32 x 32] += A[32 x 16] B[16 x 32],
 // lane l supplying row l % 32 of A (a weight row) and column l % 32 of B (an
@@ -59,65 +80,78 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 template <typename TW, int FM>
 struct TiledMain {
   static constexpr int BM = 16 * FM;
-  static constexpr int F2 = BM / 32;  // 32-row activation fragments
-  static constexpr int XQ = BM / 32;  // 16-byte activation loads per thread per stage
+  static constexpr int F2 = BM / 32;
+  static constexpr int XQ = BM / 32;
   static constexpr int XBUF = BM * kTXRow;
-  typedef typename WFrag<TW>::raw WRaw;
+  static constexpr int WBUF = 64 * WLds<TW>::ROWB;   // per wave
+  static constexpr int LDS_BYTES = 2 * XBUF + 4 * WBUF;
 
   // acc[i][j]: lane (r, h) holds y[n0w + 32 i + 8 q + 4 h + e][m0 + 32 j + r]
-  // in element 4 q + e, summed over k in [kb, kb + 64 nk).  Tile 1 is fetched
-  // unconditionally (tile 0 again when nk == 1) so the loads in flight at
-  // the loop entry match those at its back edge and the compiler's wait
-  // counts stay exact.
+  // in element 4 q + e, summed over k in [kb, kb + 64 nk).  Rows past the
+  // operands' ends are clamped to the last row (their results are never
+  // stored); loads past the last stage repeat the last stage, so the loads
+  // in flight are the same on every pass of the loop and the compiler's
+  // wait counts stay exact.
   __device__ static void run(const bf16_t* __restrict__ X, int64_t ldx, const TW* __restrict__ W,
                              int64_t ldw, int N, int Mact, int n0w, int m0, int kb, int nk,
                              f32x16 (&acc)[2][F2], char* lds) {
-    const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid >> 6;
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < F2; ++j) acc[i][j] = f32x16{};
     if (nk <= 0) return;
-    const TW* wp[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = min(n0w + 32 * i + r, N - 1);
-      wp[i] = W + int64_t(n) * ldw + kb + 8 * h;
-    }
+    constexpr int SW = int(sizeof(TW));
+    constexpr int WROWB = WLds<TW>::ROWB, NLD = WLds<TW>::NLD;
+    constexpr int LPR = 64 * SW / 16;          // lanes per row in a coalesced load (8 bf16, 4 fp8)
+    constexpr int RPI = 64 / LPR;              // rows per load instruction
     const int xr = tid >> 3, xc = tid & 7;
-    const bf16_t* xp[XQ];
+    const char* wbase = reinterpret_cast<const char*>(W);
+    const char* xbase = reinterpret_cast<const char*>(X);
+    // coalesced weight loads: instruction q covers rows RPI q .. RPI q + RPI - 1 of the wave's 64
+    const int wrow = lane / LPR, wcol = lane % LPR;
+    uint32_t woffc[NLD], xoffc[XQ];
 #pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-      const int m = min(m0 + xr + 32 * q, Mact - 1);
-      xp[q] = X + int64_t(m) * ldx + kb + 8 * xc;
-    }
+    for (int q = 0; q < NLD; ++q)
+      woffc[q] = uint32_t(min(n0w + RPI * q + wrow, N - 1)) * uint32_t(ldw) * SW + uint32_t(kb * SW + 16 * wcol);
+#pragma unroll
+    for (int q = 0; q < XQ; ++q)
+      xoffc[q] = (uint32_t(min(m0 + xr + 32 * q, Mact - 1)) * uint32_t(ldx) + uint32_t(kb + 8 * xc)) * 2u;
     char* xdst = lds + xr * kTXRow + 16 * xc;
     const char* xsrc = lds + r * kTXRow + 16 * h;
-    WRaw wr[2][4][2];
+    char* wl = lds + 2 * XBUF + wave * WBUF;
+    char* wdst = wl + wrow * WROWB + 16 * wcol;
+    const char* wsrc = wl + r * WROWB + 8 * SW * h;
+    u32x4 wr[NLD];
     u32x4 xs[XQ];
-
-    auto load_w = [&](int st, int kt) {
+    auto load_w = [&](int kt) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int q = 0; q < NLD; ++q) wr[q] = *reinterpret_cast<const u32x4*>(wbase + woffc[q] + uint32_t(kt * kTKT * SW));
+    };
+    auto store_w = [&]() {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) wr[st][s][i] = WFrag<TW>::load(wp[i] + kt * kTKT + 16 * s);
+      for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wdst + q * RPI * WROWB) = wr[q];
     };
     auto load_x = [&](int kt) {
 #pragma unroll
-      for (int q = 0; q < XQ; ++q) xs[q] = *reinterpret_cast<const u32x4*>(xp[q] + kt * kTKT);
+      for (int q = 0; q < XQ; ++q) xs[q] = *reinterpret_cast<const u32x4*>(xbase + xoffc[q] + uint32_t(kt * kTKT * 2));
     };
     auto store_x = [&](int buf) {
 #pragma unroll
       for (int q = 0; q < XQ; ++q)
         *reinterpret_cast<u32x4*>(xdst + buf * XBUF + q * 32 * kTXRow) = xs[q];
     };
-    auto compute = [&](int st, int buf) {
+    auto compute = [&](int buf) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         Frag8Bf16 wf[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) WFrag<TW>::cvt(wf[i], wr[st][s][i]);
+        for (int i = 0; i < 2; ++i) {
+          const char* p = wsrc + i * 32 * WROWB + s * 16 * SW;
+          if (SW == 2) wf[i].v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+          else fp8x8_to_frag(wf[i], *reinterpret_cast<const u32x2*>(p));
+        }
 #pragma unroll
         for (int j = 0; j < F2; ++j) {
           bf16x8 xf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
@@ -127,46 +161,31 @@ struct TiledMain {
         }
       }
     };
+    // W(kt) sits in registers at the start of stage kt and is copied to this
+    // wave's LDS region; X(kt) is in LDS buffer kt & 1.
+    load_w(0);
     load_x(0);
-    load_w(0, 0);
     store_x(0);
-    const int k1 = nk > 1 ? 1 : 0;
-    load_x(k1);
-    load_w(1, k1);
+    load_x(min(1, nk - 1));
     __syncthreads();
+    auto stage = [&](int buf, int kt) {
+      store_w();
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(min(kt + 1, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf);
+      __builtin_amdgcn_sched_barrier(0);
+      store_x(buf ^ 1);
+      load_x(min(kt + 2, nk - 1));
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
     int kt = 0;
-    for (; kt + 4 <= nk; kt += 2) {
-      compute(0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      store_x(1);
-      load_x(kt + 2);
-      load_w(0, kt + 2);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      store_x(0);
-      load_x(kt + 3);
-      load_w(1, kt + 3);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
+    for (; kt + 2 <= nk; kt += 2) {
+      stage(0, kt);
+      stage(1, kt + 1);
     }
-    const int rem = nk - kt;
-    compute(0, 0);
-    if (rem >= 2) {
-      store_x(1);
-      if (rem == 3) {
-        load_x(kt + 2);
-        load_w(0, kt + 2);
-      }
-      __syncthreads();
-      compute(1, 1);
-      if (rem == 3) {
-        store_x(0);
-        __syncthreads();
-        compute(0, 0);
-      }
-    }
+    if (kt < nk) stage(0, kt);
   }
 };
 
@@ -200,11 +219,13 @@ __device__ __forceinline__ void tiled_row_scales(const RowScale& rs, int m0, int
 }
 
 // Partial sums: P[group][split][m][n] = inv_rms[m] * scale[n] * sum_k x[m][k] W[n][k].
+// BM = 128 fits in 256 registers per lane, so two blocks share a CU and
+// cover each other's load latency.
 template <typename TW, int FM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tiled_kernel(TiledArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_tiled_kernel(TiledArgs p) {
   typedef TiledMain<TW, FM> Main;
   constexpr int BM = Main::BM, F2 = Main::F2;
-  __shared__ __attribute__((aligned(16))) char lds[2 * Main::XBUF];
+  __shared__ __attribute__((aligned(16))) char lds[Main::LDS_BYTES];
   __shared__ float inv[BM];
   int mt, nt, split, group;
   if (!tiled_tile(p, mt, nt, split, group)) return;
@@ -257,22 +278,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
-// lm_head + top-k.  Each block ranks its 256 vocabulary ids for each of its
-// BM rows and writes the row's k best keys (value desc, id asc) for that
-// vocabulary group, the same candidate layout the weight-streaming lm_head
-// writes; the merge kernel then picks each row's final k.
+// lm_head + top-k.  A block owns BM rows and a run of consecutive 256-id
+// vocabulary tiles [nt0, nt1); for each row it keeps the 16 best keys
+// (value desc, id asc) seen so far in its output slot cand[m][range][0..16),
+// which the merge kernel reduces to each row's final k.
 //
-// Selecting 16 of 256 values per row cheaply:
-//  1. a lane holds 32 values of each of its rows, in two groups of 16 (one
-//     per 32-row weight fragment); it keeps the largest and second largest
-//     of each group.  The row's 16 groups give 32 such values, and their
-//     16th largest, T, has at least 16 of the row's values >= T, so no
-//     value below T can be among the row's top 16;
-//  2. values >= T (typically ~18 of 256) are appended to the row's candidate
-//     slots in LDS; the thread owning the row insertion-sorts them into a
-//     register list of 16 keys;
-//  3. if a row had more than kTSlots values >= T, another round takes the
-//     values not yet appended whose key beats the row's current 16th key.
+// Per tile, only values that can still enter a row's list are looked at:
+//  * first tile: a lane holds 32 values of each of its rows in two groups of
+//    16 (one per 32-row weight fragment) and keeps the largest and second
+//    largest of each; the row's 16 groups give 32 such values, and their
+//    16th largest, T, has at least 16 of the row's values >= T, so nothing
+//    below T can be in the row's top 16;
+//  * later tiles: the row's current 16th key;
+// values passing (typically ~18 of 256 on the first tile, a few on later
+// ones) are compacted into the row's candidate slots in LDS (one atomic per
+// lane and row), and the thread owning the row insertion-sorts them into its
+// list.  If a row had more than kTSlots passing values, further rounds take
+// the values not yet appended whose key beats the row's new 16th key.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void sort16_desc(float (&a)[16]) {
 #pragma unroll
@@ -302,152 +324,255 @@ __device__ __forceinline__ void insert16(uint64_t (&L)[16], uint64_t x) {
 }
 
 template <typename TW, int FM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_tiled_kernel(TiledArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_tiled_kernel(TiledArgs p) {
   typedef TiledMain<TW, FM> Main;
   constexpr int BM = Main::BM, F2 = Main::F2;
-  constexpr int XB = 2 * Main::XBUF;
-  constexpr int CB = BM * kTSlots * 8;
-  constexpr int LB = XB > CB ? XB : CB;
+  constexpr int XB = Main::LDS_BYTES;
+  constexpr int CB = BM * kTSlots * 8;   // candidate slots
+  constexpr int TB = 64 * 260 * 4;       // 64 rows of tile values (overflow path)
+  constexpr int LB = XB > CB ? (XB > TB ? XB : TB) : (CB > TB ? CB : TB);
   __shared__ __attribute__((aligned(16))) char lds[LB];
   __shared__ float inv[BM];
-  __shared__ float thr[BM];
-  __shared__ uint64_t thrk[BM];
+  __shared__ float thr[BM];       // first tile: float bound T
+  __shared__ uint64_t thrk[BM];   // the row's current 16th key (0: list not full)
   __shared__ int cnt[BM];
-  int mt, nt, split, group;
-  if (!tiled_tile(p, mt, nt, split, group)) return;
+  // block -> (row tile, vocabulary range); blocks of one range are adjacent
+  const int per = gridDim.x >> 3;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= p.tiles) return;
+  const int mt = t % p.nM, rg = t / p.nM;
+  const int nt0 = rg * p.tpb, nt1 = min(p.nN, nt0 + p.tpb);
   const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
   const int m0 = mt * BM;
   if (m0 >= Mact) return;
   const int tid = threadIdx.x, wave = tid / WAVE, lane = tid & (WAVE - 1);
   const int r = lane & 31, h = lane >> 5;
-  const int n0w = nt * kTBN + 64 * wave;
   tiled_row_scales<BM>(p.rs, m0, Mact, inv);
-  f32x16 acc[2][F2];
-  Main::run(p.X, p.ldx, static_cast<const TW*>(p.W), p.ldw, p.N, Mact, n0w, m0, 0, p.K / kTKT, acc, lds);
-  __syncthreads();  // every wave is done with the activation stages
-
-  // logits (the same float32 steps as the weight-streaming lm_head); value
-  // v = 4 q + e of acc[i][j] is vocabulary id n0w + 32 i + 8 q + 4 h + e of
-  // row m0 + 32 j + r
-  float* ab = reinterpret_cast<float*>(lds);  // [BM][33]: per-group top-2 of each row
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    float s[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      s[v] = p.scale ? p.scale[min(n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3), p.N - 1)] : 1.f;
-#pragma unroll
-    for (int j = 0; j < F2; ++j) {
-      const float iv = inv[32 * j + r];
-      const int m = m0 + 32 * j + r;
-      float a = -INFINITY, b = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = acc[i][j][v];
-        x *= s[v];
-        x *= iv;
-        x = x + 0.0f;
-        acc[i][j][v] = x;
-        const bool valid = n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3) < p.N;
-        const float y = valid ? x : -INFINITY;
-        b = fmaxf(b, fminf(a, y));
-        a = fmaxf(a, y);
-      }
-      if (p.debug_logits && m < Mact) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nb = n0w + 32 * i + 8 * q + 4 * h;
-          float* dst = p.debug_logits + int64_t(m) * p.N + nb;
-          if (nb + 3 < p.N && (p.N & 3) == 0) {
-            *reinterpret_cast<f32x4*>(dst) =
-                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (nb + e < p.N) dst[e] = acc[i][j][4 * q + e];
-          }
-        }
-      }
-      const int slot = ((wave * 2 + h) * 2 + i) * 2;
-      ab[(32 * j + r) * 33 + slot] = a;
-      ab[(32 * j + r) * 33 + slot + 1] = b;
-    }
-  }
-  __syncthreads();
   if (tid < BM) {
-    float A[16], B[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      A[q] = ab[tid * 33 + 2 * q];
-      B[q] = ab[tid * 33 + 2 * q + 1];
-    }
-    sort16_desc(A);
-    sort16_desc(B);
-    // the 16 largest of the union are max(A[q], B[15 - q]); T is their minimum
-    float T = INFINITY;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) T = fminf(T, fmaxf(A[q], B[15 - q]));
-    thr[tid] = T;
-    thrk[tid] = ~0ull;
+    thrk[tid] = 0ull;
     cnt[tid] = 0;
   }
-  __syncthreads();  // ab is dead from here; its space holds the candidate slots
+  const bool owner = tid < BM && m0 + tid < Mact;
+  uint64_t* out = p.cand + (int64_t(min(m0 + tid, p.M - 1)) * p.vgroups + rg) * 16;
   uint64_t* slots = reinterpret_cast<uint64_t*>(lds);
-  uint32_t sub[F2] = {};  // values already appended: bit 16 i + v of row fragment j
-  uint64_t list[16];
+
+  for (int nt = nt0; nt < nt1; ++nt) {
+    const int n0w = nt * kTBN + 64 * wave;
+    const bool first = nt == nt0;
+    f32x16 acc[2][F2];
+    Main::run(p.X, p.ldx, static_cast<const TW*>(p.W), p.ldw, p.N, Mact, n0w, m0, 0, p.K / kTKT, acc, lds);
+    __syncthreads();  // every wave is done with the stages; LDS is free
+
+    // logits (the same float32 steps as the weight-streaming lm_head); value
+    // v = 4 q + e of acc[i][j] is vocabulary id n0w + 32 i + 8 q + 4 h + e of
+    // row m0 + 32 j + r.  Ids past the vocabulary become NaN, which passes no
+    // filter below.
+    float* ab = reinterpret_cast<float*>(lds);  // [BM][33]: per-group top-2 of each row
 #pragma unroll
-  for (int q = 0; q < 16; ++q) list[q] = 0ull;
-  for (int round = 0;; ++round) {
+    for (int i = 0; i < 2; ++i) {
+      float s[16];
 #pragma unroll
-    for (int j = 0; j < F2; ++j) {
-      const int row = 32 * j + r;
-      const float tf = thr[row];
-      const uint64_t tk = thrk[row];
+      for (int v = 0; v < 16; ++v)
+        s[v] = p.scale ? p.scale[min(n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3), p.N - 1)] : 1.f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int j = 0; j < F2; ++j) {
+        const float iv = inv[32 * j + r];
+        const int m = m0 + 32 * j + r;
+        float a = -INFINITY, b = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int n = n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-          const uint32_t bit = 1u << (16 * i + v);
-          const float x = acc[i][j][v];
-          bool pass = n < p.N && !(sub[j] & bit);
-          if (round == 0) pass = pass && x >= tf;
-          else pass = pass && rank_key(x, uint32_t(n)) > tk;
-          if (pass) {
-            const int sl = atomicAdd(&cnt[row], 1);
-            if (sl < kTSlots) {
-              slots[row * kTSlots + sl] = rank_key(x, uint32_t(n));
-              sub[j] |= bit;
+          float x = acc[i][j][v];
+          x *= s[v];
+          x *= iv;
+          x = x + 0.0f;
+          const bool valid = n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3) < p.N;
+          const float y = valid ? x : -INFINITY;
+          b = fmaxf(b, fminf(a, y));
+          a = fmaxf(a, y);
+          acc[i][j][v] = valid ? x : __builtin_nanf("");
+        }
+        if (p.debug_logits && m < Mact) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nb = n0w + 32 * i + 8 * q + 4 * h;
+            float* dst = p.debug_logits + int64_t(m) * p.N + nb;
+            if (nb + 3 < p.N && (p.N & 3) == 0) {
+              *reinterpret_cast<f32x4*>(dst) =
+                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (nb + e < p.N) dst[e] = acc[i][j][4 * q + e];
             }
           }
         }
+        if (first) {
+          const int slot = ((wave * 2 + h) * 2 + i) * 2;
+          ab[(32 * j + r) * 33 + slot] = a;
+          ab[(32 * j + r) * 33 + slot + 1] = b;
+        }
       }
     }
-    __syncthreads();
-    bool more = false;
-    if (tid < BM) {
-      const int c = cnt[tid];
-      const int nn = min(c, kTSlots);
-      for (int q = 0; q < nn; ++q) insert16(list, slots[tid * kTSlots + q]);
-      more = c > kTSlots;
-      thrk[tid] = more ? list[15] : ~0ull;
-      cnt[tid] = 0;
-    }
-    if (!__syncthreads_or(more)) break;
-  }
-  if (tid < BM && m0 + tid < Mact) {
-    uint64_t* out = p.cand + (int64_t(m0 + tid) * p.vgroups + nt) * p.k;
+    if (first) {
+      __syncthreads();
+      if (tid < BM) {
+        float A[16], B[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (q < p.k) out[q] = list[q];
+        for (int q = 0; q < 16; ++q) {
+          A[q] = ab[tid * 33 + 2 * q];
+          B[q] = ab[tid * 33 + 2 * q + 1];
+        }
+        sort16_desc(A);
+        sort16_desc(B);
+        // the 16 largest of the union are max(A[q], B[15 - q]); T is their minimum
+        float T = INFINITY;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) T = fminf(T, fmaxf(A[q], B[15 - q]));
+        thr[tid] = T;
+      }
+    }
+    __syncthreads();  // ab is dead from here; its space holds the candidate slots
+
+    // append the lane's passing values of each of its rows: one atomic per
+    // row for the lane's count, then the keys at consecutive slots
+    auto append = [&](const uint32_t (&mask)[F2]) {
+      int base[F2];
+#pragma unroll
+      for (int j = 0; j < F2; ++j) {
+        const int c = __builtin_popcount(mask[j]);
+        base[j] = c ? atomicAdd(&cnt[32 * j + r], c) : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < F2; ++j) {
+        int pos = base[j];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if ((mask[j] >> (16 * i + v)) & 1u) {
+              if (pos < kTSlots) {
+                slots[(32 * j + r) * kTSlots + pos] =
+                    rank_key(acc[i][j][v], uint32_t(n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3)));
+              }
+              ++pos;
+            }
+      }
+    };
+    {
+      uint32_t mask[F2];
+#pragma unroll
+      for (int j = 0; j < F2; ++j) {
+        const int row = 32 * j + r;
+        const float tf = thr[row];
+        const uint64_t tk = thrk[row];
+        const float tv = key_val(tk);
+        const uint32_t tlo = uint32_t(tk);
+        mask[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float x = acc[i][j][v];
+            const uint32_t nid = uint32_t(n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3));
+            bool pass;
+            if (first) pass = x >= tf;
+            else pass = tk == 0ull ? x == x : (x > tv || (x == tv && 0xFFFFFFFFu - nid > tlo));
+            mask[j] |= uint32_t(pass) << (16 * i + v);
+          }
+      }
+      append(mask);
+    }
+    // merge the row's new candidates into its list (kept in its output slot)
+    auto merge = [&](bool fresh) {
+      bool more = false;
+      if (tid < BM) {
+        uint64_t list[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) list[q] = (!fresh && owner) ? out[q] : 0ull;
+        const int c = cnt[tid];
+        const int nn = min(c, kTSlots);
+        for (int q = 0; q < nn; ++q) insert16(list, slots[tid * kTSlots + q]);
+        if (owner) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) out[q] = list[q];
+        }
+        // rows past the last activation row are never output: stop them here
+        more = owner && c > kTSlots;
+        thrk[tid] = owner ? list[15] : ~0ull;
+        cnt[tid] = 0;
+      }
+      return more;
+    };
+    // common case: no row overflowed, the tile's values are dead before the merge
+    if (!__syncthreads_or(owner && cnt[tid] > kTSlots)) {
+      merge(first);
+    } else {
+      // rare: a row had more than kTSlots values past its bound.  Rank every
+      // value of the tile exactly instead, 64 rows at a time through LDS,
+      // four threads per row, and fold the result into the rows' lists.
+      float* tv = reinterpret_cast<float*>(lds);  // [64][260]
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < F2; ++j) {
+          if ((j >> 1) != half) continue;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              tv[(32 * (j & 1) + r) * 260 + 64 * wave + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3)] = acc[i][j][v];
+        }
+        __syncthreads();
+        const int lrow = tid >> 2, qtr = tid & 3;
+        uint64_t L[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) L[q] = 0ull;
+        for (int c = 0; c < 64; ++c) {
+          const float x = tv[lrow * 260 + 64 * qtr + c];
+          const uint64_t key = rank_key(x, uint32_t(nt * kTBN + 64 * qtr + c));
+          if (x == x && key > L[15]) insert16(L, key);
+        }
+        // the row's four threads are adjacent lanes of one wave
+#pragma unroll
+        for (int d = 1; d < 4; d <<= 1) {
+          uint64_t brev[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) brev[q] = __shfl_xor(L[15 - q], d, WAVE);
+          bitonic_top<16>(L, brev);
+        }
+        const int row = 64 * half + lrow;
+        const int m = m0 + row;
+        if (qtr == 0) {
+          if (m < Mact) {
+            uint64_t* o = p.cand + (int64_t(m) * p.vgroups + rg) * 16;
+            if (!first) {
+              uint64_t brev[16];
+#pragma unroll
+              for (int q = 0; q < 16; ++q) brev[q] = o[15 - q];
+              bitonic_top<16>(L, brev);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) o[q] = L[q];
+            thrk[row] = L[15];
+          } else {
+            thrk[row] = ~0ull;
+          }
+        }
+      }
+      if (tid < BM) cnt[tid] = 0;
+    }
+    __syncthreads();  // LDS (slots, thrk) settled before the next tile's stages
   }
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-int tiled_fm(int M) { return M <= 128 ? 8 : 16; }
-int tiled_block_rows(int M) { return 16 * tiled_fm(M); }
+int tiled_block_rows(int M) {
+  (void)M;
+  return 128;
+}
 
 bool gemm_tiled_ok(int weight_dtype, int M, int K) {
   return weight_dtype != 0 && M > kTiledMinRows && K % kTKT == 0;
@@ -456,16 +581,11 @@ bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k) {
   return gemm_tiled_ok(weight_dtype, M, K) && k <= 16;
 }
 
-// The lm_head's top-k epilogue keeps every logit of the tile in registers
-// while it ranks them; at BM = 256 that does not fit, so it runs at BM = 128.
-int lmhead_tiled_block_rows() { return 128; }
-
 template <typename TW>
 static void launch_tiled_t(const TiledArgs& t, bool topk, hipStream_t s) {
   const dim3 grid(unsigned((t.tiles + 7) / 8 * 8));
   if (topk) hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 8>), grid, dim3(256), 0, s, t);
-  else if (tiled_fm(t.M) == 8) hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8>), grid, dim3(256), 0, s, t);
-  else hipLaunchKernelGGL((gemm_tiled_kernel<TW, 16>), grid, dim3(256), 0, s, t);
+  else hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8>), grid, dim3(256), 0, s, t);
 }
 
 void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s) {
@@ -485,16 +605,45 @@ void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s) {
   else launch_tiled_t<fp8_t>(t, false, s);
 }
 
+// Vocabulary tiles per lm_head block: the run with the shortest makespan,
+// counted in tiles on the 512 block slots (two per CU); ties go to the
+// shorter run (longer sweeps let the blocks that share a weight tile drift
+// apart, which costs more L2 hits than the cheaper later-tile filtering
+// saves).
+int lmhead_tiles_per_block(int M, int V) {
+  const int nM = (M + tiled_block_rows(M) - 1) / tiled_block_rows(M);
+  const int nN = (V + kTBN - 1) / kTBN;
+  int best = 1;
+  long best_cost = -1;
+  for (int tpb = 1; tpb <= 32 && tpb <= nN; ++tpb) {
+    const long blocks = long(nM) * ((nN + tpb - 1) / tpb);
+    const long cost = (blocks + 511) / 512 * tpb;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = tpb;
+    }
+  }
+  return best;
+}
+
+int lmhead_tiled_lists(int M, int V) {
+  const int nN = (V + kTBN - 1) / kTBN;
+  const int tpb = lmhead_tiles_per_block(M, V);
+  return (nN + tpb - 1) / tpb;
+}
+
 void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
   TiledArgs t{};
   t.X = static_cast<const bf16_t*>(a.X); t.ldx = a.ldx;
   t.W = a.W; t.ldw = a.ldw; t.scale = a.scale;
   t.M = a.M; t.N = a.N; t.K = a.K; t.M_dev = a.M_dev; t.rs = a.rs;
   t.splits = 1; t.k_split = a.K; t.groups = 1;
-  t.k = a.k; t.vgroups = a.groups; t.cand = a.cand; t.debug_logits = a.debug_logits;
-  t.nM = (a.M + lmhead_tiled_block_rows() - 1) / lmhead_tiled_block_rows();
+  t.k = a.k; t.cand = a.cand; t.debug_logits = a.debug_logits;
+  t.nM = (a.M + tiled_block_rows(a.M) - 1) / tiled_block_rows(a.M);
   t.nN = (a.N + kTBN - 1) / kTBN;
-  t.tiles = t.nM * t.nN;
+  t.tpb = lmhead_tiles_per_block(a.M, a.N);
+  t.vgroups = lmhead_tiled_lists(a.M, a.N);
+  t.tiles = t.nM * t.vgroups;
   if (weight_dtype == 1) launch_tiled_t<bf16_t>(t, true, s);
   else launch_tiled_t<fp8_t>(t, true, s);
 }

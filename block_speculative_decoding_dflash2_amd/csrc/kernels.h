@@ -47,8 +47,8 @@ struct LmHeadArgs {
 };
 
 struct TopkMergeArgs {
-  const uint64_t* cand;           // [M][count]
-  int count, M, k;
+  const uint64_t* cand;           // [M][count]: count / glen sorted lists of glen keys
+  int count, glen, M, k;
   const int32_t* M_dev;
   int32_t* ids; float* vals;      // [M][k]
   float multiplier, softcap;
@@ -138,6 +138,7 @@ constexpr int kTiledMinRows = 64;
 int gemm_rows_per_block(int weight_dtype, int M);
 bool gemm_tiled_ok(int weight_dtype, int M, int K);
 bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k);
+int lmhead_tiled_lists(int M, int V);
 int tiled_block_rows(int M);
 void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s);
 void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s);

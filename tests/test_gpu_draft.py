@@ -169,3 +169,28 @@ def test_draft_large_sampled(name, seqs):
         check_step(g, res, seqs)
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "medium_bf16", "medium_fp8"])
+def test_lmhead_topk_heavy_ties(name):
+    """lm_head rows that repeat five base rows make each logit row five
+    values repeated ~V/5 times: the top-k must still be exactly the (value
+    desc, id asc) order of the GPU's own logits.  On the tiled lm_head far
+    more than 32 values of a row reach the row's bound, so this runs its
+    exact-ranking fallback on every vocabulary tile."""
+    w = synth.get(name)
+    W = synth.make_weights(w)
+    rep = np.arange(w.vocab) % 5
+    W.lm_head.data[:] = W.lm_head.data[rep]
+    if W.lm_head.scale is not None:
+        W.lm_head.scale[:] = W.lm_head.scale[rep]
+    g = DraftRun(w, W=W)
+    try:
+        k = w.top_k
+        z = g.logits.reshape(-1, w.vocab)
+        ties = (z == z.max(axis=1, keepdims=True)).sum(axis=1)
+        log(f"{name}: copies of each row's maximum: min {ties.min()}, max {ties.max()}")
+        assert ties.min() > 32
+        assert topk_consistent(g.topk_ids.reshape(-1, k), g.topk_vals.reshape(-1, k), z, k)
+    finally:
+        g.close()
