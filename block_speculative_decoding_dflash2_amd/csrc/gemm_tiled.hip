@@ -21,6 +21,9 @@
 // Two epilogues: float32 split-K partial sums (the same layout the
 // weight-streaming kernels write, reduced by the consumer kernel), and the
 // lm_head's per-256-vocabulary-group top-k (see the top-k section below).
+#include <algorithm>
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -610,9 +613,14 @@ void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s) {
 // shorter run (longer sweeps let the blocks that share a weight tile drift
 // apart, which costs more L2 hits than the cheaper later-tile filtering
 // saves).
+// DFLASH2_LMHEAD_TILES_PER_BLOCK (1..64) overrides the choice.
 int lmhead_tiles_per_block(int M, int V) {
   const int nM = (M + tiled_block_rows(M) - 1) / tiled_block_rows(M);
   const int nN = (V + kTBN - 1) / kTBN;
+  if (const char* env = std::getenv("DFLASH2_LMHEAD_TILES_PER_BLOCK")) {
+    const int v = std::atoi(env);
+    if (v >= 1 && v <= 64) return std::min(v, nN);
+  }
   int best = 1;
   long best_cost = -1;
   for (int tpb = 1; tpb <= 32 && tpb <= nN; ++tpb) {

@@ -34,6 +34,11 @@
  *     bf16 (uint16 bit pattern) otherwise; "param" (embedding, conv taps,
  *     norm gains) follows act; weights of the linears follow weight_dtype
  *     (fp8 = OCP e4m3fn codes with one float32 scale per output row).
+ *   - Tuning: the environment variable DFLASH2_LMHEAD_TILES_PER_BLOCK
+ *     (1..64), read at each dflash2_draft_block call, sets how many
+ *     256-id vocabulary tiles one lm_head block sweeps when the batch has
+ *     more than 64 rows (default: chosen from the shapes).  Results do not
+ *     depend on it.
  *   - Every call returns DFLASH2_OK or an error code; on error nothing was
  *     enqueued and dflash2_last_error() (thread-local) describes it.  Device
  *     data (ids, lengths, offsets) cannot be checked on the host; kernels

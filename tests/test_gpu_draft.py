@@ -194,3 +194,30 @@ def test_lmhead_topk_heavy_ties(name):
         assert topk_consistent(g.topk_ids.reshape(-1, k), g.topk_vals.reshape(-1, k), z, k)
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name", ["medium_bf16", "medium_fp8"])
+def test_lmhead_vocabulary_sweeps(name, monkeypatch):
+    """The tiled lm_head with each block sweeping three vocabulary tiles
+    (later tiles filter against the row's running 16th key): same checks as
+    the single-tile default, plus the heavy-tie lattice."""
+    monkeypatch.setenv("DFLASH2_LMHEAD_TILES_PER_BLOCK", "3")
+    w = synth.get(name)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
+    W = synth.make_weights(w)
+    rep = np.arange(w.vocab) % 5
+    W.lm_head.data[:] = W.lm_head.data[rep]
+    if W.lm_head.scale is not None:
+        W.lm_head.scale[:] = W.lm_head.scale[rep]
+    g = DraftRun(w, W=W)
+    try:
+        k = w.top_k
+        z = g.logits.reshape(-1, w.vocab)
+        assert topk_consistent(g.topk_ids.reshape(-1, k), g.topk_vals.reshape(-1, k), z, k)
+    finally:
+        g.close()
