@@ -3,6 +3,7 @@
 // of one draft step.  No device memory is allocated and no call
 // synchronises; everything is enqueued on the caller's stream.
 #include <algorithm>
+#include <cstdlib>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -77,21 +78,26 @@ struct Split {
   int splits = 1, k_split = 0;
 };
 
-constexpr int kCUs = 256;
+constexpr int kTiledSlots = 512;  // tiled-GEMM blocks resident at once: two per CU on 256 CUs
 
 Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
   Split s;
   if (gemm_tiled_ok(dtype, M, K)) {
     // compute-bound tiles: pick the split count with the shortest makespan,
-    // counting waves of one tile per CU, each costing its k range plus a
-    // fixed epilogue/prologue cost of about 512 k; ties go to fewer splits
+    // counting waves of kTiledSlots resident tiles, each costing its k range
+    // plus a fixed epilogue/prologue cost of about 512 k; ties go to fewer
+    // splits
     const int64_t tiles = cdiv(M, tiled_block_rows(M)) * cdiv(N, 256) * groups;
-    int best = 1;
+    int best = 1, max_splits = 16;
+    if (const char* env = std::getenv("DFLASH2_TILED_MAX_SPLITS")) {
+      const int v = std::atoi(env);
+      if (v >= 1 && v <= 16) max_splits = v;
+    }
     double best_cost = 1e300;
-    for (int S = 1; S <= 16; ++S) {
+    for (int S = 1; S <= max_splits; ++S) {
       const int64_t ks = cdiv(cdiv(K, S), 64) * 64;
       if (cdiv(K, ks) != S) continue;
-      const double cost = double(cdiv(tiles * S, kCUs)) * double(ks + 512);
+      const double cost = double(cdiv(tiles * S, kTiledSlots)) * double(ks + 512);
       if (cost < best_cost * 0.97) {
         best_cost = cost;
         best = S;
@@ -349,17 +355,23 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
   char* vc = static_cast<char*>(v_cache);
   dflash2_status st;
 
+  // returns whether `epi` was applied inside the GEMM (else the caller runs
+  // the consumer kernel on the partial sums)
   auto gemm = [&](const void* X, int64_t ldx, const void* W, const float* scale, int M,
-                  const int32_t* M_dev, int N, int K, const Split& sp, float* out, const RowScale& rs) {
+                  const int32_t* M_dev, int N, int K, const Split& sp, float* out, const RowScale& rs,
+                  const GemmEpi* epi = nullptr) {
     GemmArgs a{};
     a.rs = rs;
+    if (epi) a.epi = *epi;
     a.X = X; a.ldx = ldx; a.W = W; a.ldw = K; a.scale = scale;
     a.P = out; a.ldp = N; a.split_stride = int64_t(M) * N;
     a.M = M; a.N = N; a.K = K; a.M_dev = M_dev;
     a.splits = sp.splits; a.k_split = sp.k_split; a.groups = 1;
     const int64_t bytes = int64_t(N) * K * wb + (scale ? int64_t(N) * 4 : 0) + int64_t(M) * K * ab +
                           int64_t(M) * N * 4;
+    const bool fused = epi && gemm_epi_fusable(dt, a);
     traced(stream, DFLASH2_K_GEMM, bytes, 2 * int64_t(M) * N * K, [&] { launch_gemm(dt, a, stream); });
+    return fused;
   };
   auto norm = [&](int rows, const int32_t* rows_dev, int nbs, const void* embed, const float* base,
                   const float* prt, const Split* sp, int64_t pstride, const void* conv,
@@ -425,13 +437,18 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
     const bool fp8 = dt == DFLASH2_FP8_E4M3;
     void* kl = kc + l * cache_layer * ab;
     void* vl = vc + l * cache_layer * ab;
-    gemm(nbuf, H, L.wqkv, fp8 ? L.wqkv_scale : nullptr, P.M, nullptr, qkvd, H, P.qkv, parts, normed);
-    QkvEpiArgs qa{};
-    qa.parts = parts; qa.splits = P.qkv.splits; qa.split_stride = int64_t(P.M) * qkvd; qa.ldp = qkvd;
-    qa.ctx_lens = ctx_lens; qa.M = P.M; qa.bs = bs; qa.nq = nq; qa.nkv = nkv; qa.d = d;
-    qa.Lmax = c.max_context; qa.theta = c.rope_theta; qa.q_out = qbuf; qa.k_layer = kl; qa.v_layer = vl;
-    traced(stream, DFLASH2_K_QKV_EPILOGUE, int64_t(P.M) * qkvd * (4 * P.qkv.splits + ab), 0,
-           [&] { launch_qkv_epilogue(f32, qa, stream); });
+    GemmEpi qe{};
+    qe.kind = EPI_QKV;
+    qe.ctx_lens = ctx_lens; qe.bs = bs; qe.nq = nq; qe.nkv = nkv; qe.d = d; qe.Lmax = c.max_context;
+    qe.theta = c.rope_theta; qe.q_out = qbuf; qe.k_layer = kl; qe.v_layer = vl;
+    if (!gemm(nbuf, H, L.wqkv, fp8 ? L.wqkv_scale : nullptr, P.M, nullptr, qkvd, H, P.qkv, parts, normed, &qe)) {
+      QkvEpiArgs qa{};
+      qa.parts = parts; qa.splits = P.qkv.splits; qa.split_stride = int64_t(P.M) * qkvd; qa.ldp = qkvd;
+      qa.ctx_lens = ctx_lens; qa.M = P.M; qa.bs = bs; qa.nq = nq; qa.nkv = nkv; qa.d = d;
+      qa.Lmax = c.max_context; qa.theta = c.rope_theta; qa.q_out = qbuf; qa.k_layer = kl; qa.v_layer = vl;
+      traced(stream, DFLASH2_K_QKV_EPILOGUE, int64_t(P.M) * qkvd * (4 * P.qkv.splits + ab), 0,
+             [&] { launch_qkv_epilogue(f32, qa, stream); });
+    }
 
     AttnArgs aa{};
     aa.q = qbuf; aa.k_layer = kl; aa.v_layer = vl; aa.ctx_lens = ctx_lens;
@@ -456,13 +473,17 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
     gemm(obuf, qd, L.wo, fp8 ? L.wo_scale : nullptr, P.M, nullptr, H, qd, P.o, parts, plain);
     norm(P.M, nullptr, bs, nullptr, h0, parts, &P.o, int64_t(P.M) * H, L.conv_ffn, L.ffn_norm, h1,
          nbuf, 0);
-    gemm(nbuf, H, L.w_gate_up, fp8 ? L.w_gate_up_scale : nullptr, P.M, nullptr, 2 * F, H, P.gu, parts,
-         normed);
-    SwigluArgs sa{};
-    sa.parts = parts; sa.splits = P.gu.splits; sa.split_stride = int64_t(P.M) * 2 * F; sa.ldp = 2 * F;
-    sa.M = P.M; sa.F = F; sa.out = abuf;
-    traced(stream, DFLASH2_K_SWIGLU, int64_t(P.M) * F * (8 * P.gu.splits + ab), 0,
-           [&] { launch_swiglu(f32, sa, stream); });
+    GemmEpi se{};
+    se.kind = EPI_SWIGLU;
+    se.act_out = abuf; se.F = F;
+    if (!gemm(nbuf, H, L.w_gate_up, fp8 ? L.w_gate_up_scale : nullptr, P.M, nullptr, 2 * F, H, P.gu, parts,
+              normed, &se)) {
+      SwigluArgs sa{};
+      sa.parts = parts; sa.splits = P.gu.splits; sa.split_stride = int64_t(P.M) * 2 * F; sa.ldp = 2 * F;
+      sa.M = P.M; sa.F = F; sa.out = abuf;
+      traced(stream, DFLASH2_K_SWIGLU, int64_t(P.M) * F * (8 * P.gu.splits + ab), 0,
+             [&] { launch_swiglu(f32, sa, stream); });
+    }
     gemm(abuf, F, L.w_down, fp8 ? L.w_down_scale : nullptr, P.M, nullptr, H, F, P.down, parts, plain);
     if (l + 1 < c.num_layers) {
       const dflash2_layer_weights& Ln = handle->layers[l + 1];

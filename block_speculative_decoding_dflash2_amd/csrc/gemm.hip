@@ -405,6 +405,12 @@ int gemm_rows_per_block(int weight_dtype, int M) {
   return 128;
 }
 
+bool tiled_epi_fusable(const GemmArgs& a);
+
+bool gemm_epi_fusable(int weight_dtype, const GemmArgs& a) {
+  return weight_dtype != 0 && gemm_tiled_ok(weight_dtype, a.M, a.K) && tiled_epi_fusable(a);
+}
+
 void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s) {
   if (gemm_tiled_ok(weight_dtype, a.M, a.K)) {
     launch_gemm_tiled(weight_dtype, a, s);

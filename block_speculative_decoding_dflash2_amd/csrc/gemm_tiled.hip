@@ -54,6 +54,7 @@ struct TiledArgs {
   int k, vgroups; uint64_t* cand; float* debug_logits;  // top-k epilogue
   int nM, nN, tiles;
   int tpb;                                    // vocabulary tiles per lm_head block
+  GemmEpi epi;                                // gemm_tiled_kernel consumer (one K split)
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -221,15 +222,25 @@ __device__ __forceinline__ void tiled_row_scales(const RowScale& rs, int m0, int
   }
 }
 
-// Partial sums: P[group][split][m][n] = inv_rms[m] * scale[n] * sum_k x[m][k] W[n][k].
+// Partial sums: P[group][split][m][n] = inv_rms[m] * scale[n] * sum_k x[m][k] W[n][k],
+// or (one K split, EPI != EPI_NONE) that value's consumer applied in place:
+//  * EPI_SWIGLU: block nt holds gate rows [128 nt, 128 nt + 128) in waves 0-1
+//    and the matching up rows F + ... in waves 2-3; the up values go through
+//    LDS and waves 0-1 write SiLU(gate) * up;
+//  * EPI_QKV: the tile's columns are whole heads (d = 64 or 128); RoPE pairs
+//    (c, c + d/2) sit in one lane (d = 64) or in waves 2k and 2k + 1
+//    (d = 128, the odd wave's values go through LDS); q heads go to q_out,
+//    k and v heads to this layer's cache rows.
 // BM = 128 fits in 256 registers per lane, so two blocks share a CU and
 // cover each other's load latency.
-template <typename TW, int FM>
+template <typename TW, int FM, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_tiled_kernel(TiledArgs p) {
   typedef TiledMain<TW, FM> Main;
   constexpr int BM = Main::BM, F2 = Main::F2;
-  __shared__ __attribute__((aligned(16))) char lds[Main::LDS_BYTES];
+  constexpr int EB = EPI == EPI_NONE ? 0 : BM * 132 * 4;  // exchange buffer [BM][132] floats
+  __shared__ __attribute__((aligned(16))) char lds[Main::LDS_BYTES > EB ? Main::LDS_BYTES : EB];
   __shared__ float inv[BM];
+  __shared__ double inv_freq[EPI == EPI_QKV ? 64 : 1];
   int mt, nt, split, group;
   if (!tiled_tile(p, mt, nt, split, group)) return;
   const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
@@ -237,23 +248,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (m0 >= Mact) return;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
   const int r = lane & 31, h = lane >> 5;
-  const int n0w = nt * kTBN + 64 * wave;
+  int n0w = nt * kTBN + 64 * wave;
+  if (EPI == EPI_SWIGLU) n0w = (wave < 2 ? 0 : p.epi.F) + 128 * nt + 64 * (wave & 1);
   const TW* W = static_cast<const TW*>(p.groups > 1 ? p.Wg[group] : p.W);
   const float* scale = p.groups > 1 ? p.Sg[group] : p.scale;
   const int kb = split * p.k_split;
   const int nk = (min(p.K, kb + p.k_split) - kb) / kTKT;
   tiled_row_scales<BM>(p.rs, m0, Mact, inv);  // visible after the main loop's barriers
+  if (EPI == EPI_QKV && threadIdx.x < p.epi.d / 2)
+    inv_freq[threadIdx.x] = pow(double(p.epi.theta), -2.0 * double(threadIdx.x) / double(p.epi.d));
   f32x16 acc[2][F2];
   Main::run(p.X, p.ldx, W, p.ldw, p.N, Mact, n0w, m0, kb, nk, acc, lds);
   __syncthreads();
-  float* P = p.P + int64_t(group) * p.group_stride + int64_t(split) * p.split_stride;
-  // lane (r, h) holds y[n0w + 32 i + 8 q + 4 h + e][m0 + 32 j + r] in acc[i][j][4 q + e]
+  // lane (r, h) holds y[n0w + 32 i + 8 q + 4 h + e][m0 + 32 j + r] in acc[i][j][4 q + e];
+  // scale it to the stored value
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int nb = n0w + 32 * i + 8 * q + 4 * h;
-      if (nb >= p.N) continue;
       float s[4] = {1.f, 1.f, 1.f, 1.f};
       if (scale) {
 #pragma unroll
@@ -261,19 +274,154 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
 #pragma unroll
       for (int j = 0; j < F2; ++j) {
+        const float iv = inv[32 * j + r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = (acc[i][j][4 * q + e] * s[e]) * iv;
+      }
+    }
+  }
+  if (EPI == EPI_NONE) {
+    float* P = p.P + int64_t(group) * p.group_stride + int64_t(split) * p.split_stride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nb = n0w + 32 * i + 8 * q + 4 * h;
+        if (nb >= p.N) continue;
+#pragma unroll
+        for (int j = 0; j < F2; ++j) {
+          const int m = m0 + 32 * j + r;
+          if (m >= Mact) continue;
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          float* dst = P + int64_t(m) * p.ldp + nb;
+          if (nb + 3 < p.N && (p.ldp & 3) == 0) {
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (nb + e < p.N) dst[e] = v[e];
+          }
+        }
+      }
+    }
+    return;
+  }
+  // exchange: waves 2-3 (up rows, or the second half of each 128-wide head)
+  // publish their values at [row][column within the pair of waves]
+  float* xb = reinterpret_cast<float*>(lds);
+  const bool second = EPI == EPI_SWIGLU ? wave >= 2 : (p.epi.d == 128 && (wave & 1));
+  const bool exchange = EPI == EPI_SWIGLU || p.epi.d == 128;
+  if (exchange && second) {
+    const int cw = EPI == EPI_SWIGLU ? 64 * (wave & 1) : 64 * (wave >> 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < F2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          xb[(32 * j + r) * 132 + cw + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3)] = acc[i][j][v];
+  }
+  __syncthreads();
+  if (exchange && second) return;
+  const int cw = EPI == EPI_SWIGLU ? 64 * (wave & 1) : 64 * (wave >> 1);
+  if (EPI == EPI_SWIGLU) {
+    const int F = p.epi.F;
+    bf16_t* out = static_cast<bf16_t*>(p.epi.act_out);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = 128 * nt + 64 * (wave & 1) + 32 * i + 8 * q + 4 * h;
+#pragma unroll
+        for (int j = 0; j < F2; ++j) {
+          const int m = m0 + 32 * j + r;
+          if (m >= Mact) continue;
+          uint32_t o[2];
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            float y[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const float gt = acc[i][j][4 * q + e + u];
+              const float up = xb[(32 * j + r) * 132 + cw + 32 * i + 8 * q + 4 * h + e + u];
+              y[u] = gt / (1.0f + expf(-gt)) * up;
+            }
+            o[e / 2] = uint32_t(f32_to_bf16(y[0])) | (uint32_t(f32_to_bf16(y[1])) << 16);
+          }
+          bf16_t* dst = out + int64_t(m) * F + f;
+          if (f + 3 < F && (F & 3) == 0) {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{o[0], o[1]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (f + e < F) dst[e] = bf16_t(o[e / 2] >> (16 * (e & 1)));
+          }
+        }
+      }
+    return;
+  }
+  // EPI_QKV: this lane's columns c (first half of a head) pair with c + d/2
+  const GemmEpi& e = p.epi;
+  const int d = e.d, half = d / 2, nh = e.nq + 2 * e.nkv;
+  bf16_t* qo = static_cast<bf16_t*>(e.q_out);
+  bf16_t* kc = static_cast<bf16_t*>(e.k_layer);
+  bf16_t* vc = static_cast<bf16_t*>(e.v_layer);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (d == 64 && i == 1) continue;  // d = 64: the pair is (i = 0, i = 1) of this lane
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c0 = n0w + 32 * i + 8 * q + 4 * h;  // output column of the first element
+      const int head = c0 / d, ci = c0 % d;          // ci < d/2
+      if (head >= nh) continue;
+#pragma unroll
+      for (int j = 0; j < F2; ++j) {
         const int m = m0 + 32 * j + r;
         if (m >= Mact) continue;
-        const float iv = inv[32 * j + r];
-        f32x4 v;
+        const int b = m / e.bs, t = m % e.bs;
+        const int pos = e.ctx_lens[b] + t;
+        float y0[4], y1[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (acc[i][j][4 * q + e] * s[e]) * iv;
-        float* dst = P + int64_t(m) * p.ldp + nb;
-        if (nb + 3 < p.N && (p.ldp & 3) == 0) {
-          *reinterpret_cast<f32x4*>(dst) = v;
-        } else {
+        for (int u = 0; u < 4; ++u) {
+          const float x0 = acc[i][j][4 * q + u];
+          const float x1 = d == 64 ? acc[1][j][4 * q + u]
+                                   : xb[(32 * j + r) * 132 + cw + 32 * i + 8 * q + 4 * h + u];
+          if (head < e.nq + e.nkv) {
+            // angle in double, reduced to [-pi, pi], then float sine and cosine
+            const double ang = double(pos) * inv_freq[ci + u];
+            const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+            float sn, cs;
+            sincosf(float(red), &sn, &cs);
+            y0[u] = x0 * cs - x1 * sn;
+            y1[u] = x1 * cs + x0 * sn;
+          } else {
+            y0[u] = x0;
+            y1[u] = x1;
+          }
+        }
+        const u32x2 lo = {uint32_t(f32_to_bf16(y0[0])) | (uint32_t(f32_to_bf16(y0[1])) << 16),
+                          uint32_t(f32_to_bf16(y0[2])) | (uint32_t(f32_to_bf16(y0[3])) << 16)};
+        const u32x2 hi = {uint32_t(f32_to_bf16(y1[0])) | (uint32_t(f32_to_bf16(y1[1])) << 16),
+                          uint32_t(f32_to_bf16(y1[2])) | (uint32_t(f32_to_bf16(y1[3])) << 16)};
+        if (head < e.nq) {
+          bf16_t* dst = qo + (int64_t(m) * e.nq + head) * d;
+          *reinterpret_cast<u32x2*>(dst + ci) = lo;
+          *reinterpret_cast<u32x2*>(dst + ci + half) = hi;
+        } else if (pos >= 0 && pos < e.Lmax) {
+          if (head < e.nq + e.nkv) {
+            const int g = head - e.nq;
+            bf16_t* dst = kc + ((int64_t(b) * e.nkv + g) * e.Lmax + pos) * d;
+            *reinterpret_cast<u32x2*>(dst + ci) = lo;
+            *reinterpret_cast<u32x2*>(dst + ci + half) = hi;
+          } else {
+            const int g = head - e.nq - e.nkv;
+            bf16_t* dst = vc + (int64_t(b) * e.nkv + g) * d * e.Lmax + pos;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (nb + e < p.N) dst[e] = v[e];
+            for (int u = 0; u < 4; ++u) {
+              dst[int64_t(ci + u) * e.Lmax] = f32_to_bf16(y0[u]);
+              dst[int64_t(ci + half + u) * e.Lmax] = f32_to_bf16(y1[u]);
+            }
+          }
         }
       }
     }
@@ -588,7 +736,16 @@ template <typename TW>
 static void launch_tiled_t(const TiledArgs& t, bool topk, hipStream_t s) {
   const dim3 grid(unsigned((t.tiles + 7) / 8 * 8));
   if (topk) hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 8>), grid, dim3(256), 0, s, t);
-  else hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8>), grid, dim3(256), 0, s, t);
+  else if (t.epi.kind == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8, EPI_SWIGLU>), grid, dim3(256), 0, s, t);
+  else if (t.epi.kind == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8, EPI_QKV>), grid, dim3(256), 0, s, t);
+  else hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8, EPI_NONE>), grid, dim3(256), 0, s, t);
+}
+
+bool tiled_epi_fusable(const GemmArgs& a) {
+  if (a.epi.kind == EPI_NONE || a.splits != 1 || a.groups > 1 || a.M_dev) return false;
+  if (a.epi.kind == EPI_SWIGLU) return a.N == 2 * a.epi.F && a.epi.act_out;
+  if (a.epi.kind == EPI_QKV) return (a.epi.d == 64 || a.epi.d == 128) && a.N % a.epi.d == 0;
+  return false;
 }
 
 void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s) {
@@ -601,8 +758,10 @@ void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s) {
   for (int i = 0; i < kMaxGroups; ++i) { t.Wg[i] = a.Wg[i]; t.Sg[i] = a.Sg[i]; }
   t.group_stride = a.group_stride;
   t.P = a.P; t.ldp = a.ldp; t.split_stride = a.split_stride;
+  t.epi = a.epi;
+  if (!tiled_epi_fusable(a)) t.epi.kind = EPI_NONE;
   t.nM = (a.M + tiled_block_rows(a.M) - 1) / tiled_block_rows(a.M);
-  t.nN = (a.N + kTBN - 1) / kTBN;
+  t.nN = t.epi.kind == EPI_SWIGLU ? (a.epi.F + 127) / 128 : (a.N + kTBN - 1) / kTBN;
   t.tiles = t.nM * t.nN * t.splits * t.groups;
   if (weight_dtype == 1) launch_tiled_t<bf16_t>(t, false, s);
   else launch_tiled_t<fp8_t>(t, false, s);

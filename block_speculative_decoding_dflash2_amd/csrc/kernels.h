@@ -14,6 +14,19 @@ struct RowScale {
   const float* sumsq; int blocks; float inv_width; float eps;
 };
 
+// Consumer applied in the GEMM epilogue instead of writing partial sums
+// (LDS-tiled path with one K split: each block owns whole output values).
+enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_QKV = 2 };
+struct GemmEpi {
+  int kind;
+  // EPI_SWIGLU: act[m][f] = SiLU(gate) * up, gate = output column f, up = F + f
+  void* act_out; int F;
+  // EPI_QKV: RoPE on q and k heads (position ctx_lens[m / bs] + m % bs);
+  // q -> q_out [M][nq][d], k -> k_layer rows, v -> v_layer rows (transposed)
+  const int32_t* ctx_lens; int bs, nq, nkv, d, Lmax; float theta;
+  void* q_out; void* k_layer; void* v_layer;
+};
+
 // y[s][m][n] = rowscale[m] * sum_{k in split s} X[m][k] * W[n][k]  (* scale[n])
 struct GemmArgs {
   const void* X; int64_t ldx;     // [M][K] act
@@ -31,6 +44,7 @@ struct GemmArgs {
   const void* Wg[kMaxGroups];
   const float* Sg[kMaxGroups];
   int64_t group_stride;
+  GemmEpi epi;                    // EPI_NONE: write partial sums
 };
 
 struct LmHeadArgs {
@@ -143,6 +157,9 @@ int tiled_block_rows(int M);
 void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s);
 void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s);
 void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s);
+// Whether launch_gemm applies a.epi itself (else the caller runs the
+// consumer kernel on the partial sums, which are then written).
+bool gemm_epi_fusable(int weight_dtype, const GemmArgs& a);
 void launch_lmhead_topk(int weight_dtype, const LmHeadArgs& a, hipStream_t s);
 void launch_topk_merge(const TopkMergeArgs& a, hipStream_t s);
 int norm_col_blocks(int H);

@@ -37,8 +37,11 @@
  *   - Tuning: the environment variable DFLASH2_LMHEAD_TILES_PER_BLOCK
  *     (1..64), read at each dflash2_draft_block call, sets how many
  *     256-id vocabulary tiles one lm_head block sweeps when the batch has
- *     more than 64 rows (default: chosen from the shapes).  Results do not
- *     depend on it.
+ *     more than 64 rows (default: chosen from the shapes), and
+ *     DFLASH2_TILED_MAX_SPLITS (1..16), read by dflash2_workspace_size and
+ *     dflash2_draft_block, caps the K splits of those batches' linears (one
+ *     split lets the GEMM apply SwiGLU and the QKV RoPE itself).  Results
+ *     agree to rounding either way.
  *   - Every call returns DFLASH2_OK or an error code; on error nothing was
  *     enqueued and dflash2_last_error() (thread-local) describes it.  Device
  *     data (ids, lengths, offsets) cannot be checked on the host; kernels

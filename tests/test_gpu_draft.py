@@ -221,3 +221,17 @@ def test_lmhead_vocabulary_sweeps(name, monkeypatch):
         assert topk_consistent(g.topk_ids.reshape(-1, k), g.topk_vals.reshape(-1, k), z, k)
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name", ["medium_bf16", "medium_fp8"])
+def test_draft_tiled_single_split(name, monkeypatch):
+    """Tiled GEMMs with one K split, so gate/up and QKV apply SwiGLU and the
+    RoPE / cache stores in their own epilogue: same checks as the default."""
+    monkeypatch.setenv("DFLASH2_TILED_MAX_SPLITS", "1")
+    w = synth.get(name)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
