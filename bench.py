@@ -32,16 +32,25 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the kernel sources; a traffic measurement is only used
-    while the kernels are unchanged since it was taken."""
+# Sources that define each traced kernel kind (its kernel code, device
+# helpers and argument structs).
+KERNEL_SOURCES = {
+    "gemm": ["gemm.hip", "gemm_tiled.hip", "common.h", "kernels.h"],
+    "lmhead_topk": ["gemm.hip", "gemm_tiled.hip", "common.h", "kernels.h"],
+    "attention": ["attention.hip", "common.h", "kernels.h"],
+}
+
+
+def kernel_source_hash(kernel: str = "gemm") -> str:
+    """sha256 over the sources of one kernel kind; a traffic measurement is
+    only used while that kernel is unchanged since it was taken."""
     import hashlib
     csrc = os.path.join(ROOT, "block_speculative_decoding_dflash2_amd", "csrc")
+    names = KERNEL_SOURCES.get(kernel) or sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in sorted(names):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
 
@@ -54,7 +63,7 @@ def measured_traffic(workload: str, kernel: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 

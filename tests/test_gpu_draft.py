@@ -235,3 +235,16 @@ def test_draft_tiled_single_split(name, monkeypatch):
         check_step(g, res, range(w.batch))
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name,window", [("small_bf16", 64), ("medium_fp8", 100), ("small_fp32", 33)])
+def test_draft_sliding_window(name, window):
+    """draft_sliding_window: attention reaches back `window` context rows;
+    sequences both shorter and longer than the window."""
+    w = synth.get(name).replace(sliding_window=window)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()

@@ -169,3 +169,29 @@ def test_step_runs_tiny_and_is_consistent():
         assert np.array_equal(res["topk_vals"][0, t], z32[0, t, ids])
         assert np.all(np.diff(res["topk_vals"][0, t]) <= 0)
     assert 0 <= res["accepted"][0] <= P
+
+
+def test_sliding_window_reaches_back_exactly_w_rows():
+    """[AM §Key Config Fields, draft_sliding_window] with window W the block
+    attends to context positions L - W .. L - 1 only: rewriting older cache
+    rows leaves the logits unchanged, rewriting the oldest row inside the
+    window changes them, and W >= L is the same as no window."""
+    w = W0.replace(batch=1, ctx=(24, 24))
+    W, inp = _setup(w)
+    kc, vc = O.new_cache(w, 1, inp.k_ctx, inp.v_ctx)
+    O.append_context(w, W, kc, vc, inp.taps, inp.new_offsets, inp.ctx_lens)
+    L = int(inp.ctx_lens[0])
+    full = O.draft_block(w, W, kc, vc, inp.anchors, inp.ctx_lens)["zeta"]
+    assert np.array_equal(full, O.draft_block(w.replace(sliding_window=L), W, kc, vc, inp.anchors,
+                                              inp.ctx_lens)["zeta"])
+    wl = w.replace(sliding_window=10)
+    a = O.draft_block(wl, W, kc, vc, inp.anchors, inp.ctx_lens)["zeta"]
+    rng = np.random.default_rng(5)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[:, :, :, :L - 10] = rng.standard_normal(kc2[:, :, :, :L - 10].shape)
+    vc2[:, :, :, :L - 10] = rng.standard_normal(vc2[:, :, :, :L - 10].shape)
+    assert np.array_equal(a, O.draft_block(wl, W, kc2, vc2, inp.anchors, inp.ctx_lens)["zeta"])
+    kc3 = kc.copy()
+    kc3[:, :, :, L - 10] += 1.0
+    assert not np.allclose(a, O.draft_block(wl, W, kc3, vc, inp.anchors, inp.ctx_lens)["zeta"])
+    assert not np.allclose(a, full)
