@@ -504,7 +504,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     cnt[tid] = 0;
   }
   const bool owner = tid < BM && m0 + tid < Mact;
-  uint64_t* out = p.cand + (int64_t(min(m0 + tid, p.M - 1)) * p.vgroups + rg) * 16;
+  static_assert(2 * BM == 256, "two threads per row in the ranking steps");
   uint64_t* slots = reinterpret_cast<uint64_t*>(lds);
 
   for (int nt = nt0; nt < nt1; ++nt) {
@@ -565,22 +565,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     if (first) {
+      // two adjacent lanes per row: one sorts the group maxima A, the other
+      // the second maxima B; the 16 largest of the union are
+      // max(A[q], B[15 - q]), and T is their minimum
       __syncthreads();
-      if (tid < BM) {
-        float A[16], B[16];
+      const int row = tid >> 1, half = tid & 1;
+      float L[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          A[q] = ab[tid * 33 + 2 * q];
-          B[q] = ab[tid * 33 + 2 * q + 1];
-        }
-        sort16_desc(A);
-        sort16_desc(B);
-        // the 16 largest of the union are max(A[q], B[15 - q]); T is their minimum
-        float T = INFINITY;
+      for (int q = 0; q < 16; ++q) L[q] = ab[row * 33 + 2 * q + half];
+      sort16_desc(L);
+      float T = INFINITY;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) T = fminf(T, fmaxf(A[q], B[15 - q]));
-        thr[tid] = T;
-      }
+      for (int q = 0; q < 16; ++q) T = fminf(T, fmaxf(L[q], __shfl_xor(L[15 - q], 1, WAVE)));
+      if (half == 0) thr[row] = T;
     }
     __syncthreads();  // ab is dead from here; its space holds the candidate slots
 
@@ -634,23 +631,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       append(mask);
     }
     // merge the row's new candidates into its list (kept in its output slot)
+    // (two adjacent lanes per row: each inserts every other candidate, the
+    // first also the row's list so far, then the two lists are merged)
     auto merge = [&](bool fresh) {
+      const int row = tid >> 1, half = tid & 1;
+      const bool own = m0 + row < Mact;
+      uint64_t* o = p.cand + (int64_t(min(m0 + row, p.M - 1)) * p.vgroups + rg) * 16;
+      uint64_t list[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) list[q] = (!fresh && own && half == 0) ? o[q] : 0ull;
+      const int c = cnt[row];
+      const int nn = min(c, kTSlots);
+      for (int q = half; q < nn; q += 2) insert16(list, slots[row * kTSlots + q]);
+      uint64_t brev[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) brev[q] = __shfl_xor(list[15 - q], 1, WAVE);
+      bitonic_top<16>(list, brev);
       bool more = false;
-      if (tid < BM) {
-        uint64_t list[16];
+      if (half == 0) {
+        if (own) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) list[q] = (!fresh && owner) ? out[q] : 0ull;
-        const int c = cnt[tid];
-        const int nn = min(c, kTSlots);
-        for (int q = 0; q < nn; ++q) insert16(list, slots[tid * kTSlots + q]);
-        if (owner) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) out[q] = list[q];
+          for (int q = 0; q < 16; ++q) o[q] = list[q];
         }
         // rows past the last activation row are never output: stop them here
-        more = owner && c > kTSlots;
-        thrk[tid] = owner ? list[15] : ~0ull;
-        cnt[tid] = 0;
+        more = own && c > kTSlots;
+        thrk[row] = own ? list[15] : ~0ull;
+        cnt[row] = 0;
       }
       return more;
     };
