@@ -2,8 +2,9 @@
 "DFlash2 Speculative Decoding", section "Observe Acceptance", metrics
 fields table): drafts proposed per step, steps, drafted and accepted
 totals, acceptance rate = accepted / drafted, mean acceptance length =
-1 + accepted / steps (the verified token counts), and a histogram of
-accepted drafts per step over 0..num_spec_tokens."""
+1 + accepted / steps (the verified token counts), a histogram of accepted
+drafts per step over 0..num_spec_tokens, and the acceptance rate by draft
+position (the fraction of steps whose draft i was accepted)."""
 from __future__ import annotations
 
 from typing import Dict, Iterable, List
@@ -27,4 +28,6 @@ def speculative_metrics(per_step_accepted: Iterable[int], num_spec_tokens: int) 
         "draft_acceptance_rate": accepted / drafted if drafted else 0.0,
         "mean_acceptance_length": 1.0 + accepted / steps if steps else 0.0,
         "acceptance_histogram": hist,
+        "acceptance_by_position": [sum(1 for a in acc if a > i) / steps if steps else 0.0
+                                   for i in range(num_spec_tokens)],
     }

@@ -445,3 +445,55 @@ def step(w, W, inp, target_logits_fn=None) -> Dict[str, np.ndarray]:
         out.update(verify_accept(sel["drafts"], tl))
         out["target_logits"] = tl
     return out
+
+
+# ----------------------------------------------------------------------------
+# The steps either side of the path: a multi-step decode loop.
+# ----------------------------------------------------------------------------
+
+
+def decode_loop(w, W, inp, steps: int, target_logits_fn, verified_taps_fn) -> Dict[str, list]:
+    """`steps` draft -> select -> verify rounds with the state carried over.
+
+    [LC §Prerequisites and §Complete Runnable Code: the target scores the
+    last verified token plus the drafts in one batch, the accepted prefix
+    and the target's own next token are emitted; NIM §Observe Acceptance:
+    per-step accepted counts and the verified token; AM §What is DFlash?:
+    the draft is conditioned on the target's hidden states of verified
+    positions.]  Reading Q2: after a step that accepts a drafts, the
+    target has verified the anchor and those a drafts, so their a + 1
+    positions (L .. L + a) are appended next step, the context grows to
+    L + a + 1 and the target's next token (the bonus) is the new anchor.
+    The block's own keys are never kept (no draft-side rollback).
+
+    target_logits_fn(step, drafts) -> [B, bs, V] float32 verifier logits;
+    verified_taps_fn(starts, counts) -> (taps Tensor, offsets) for positions
+    starts[b] .. starts[b] + counts[b] - 1.  Returns per-step lists of
+    drafts, accepted, bonus and ctx_lens (before the step)."""
+    B = len(inp.anchors)
+    k_cache, v_cache = new_cache(w, B, inp.k_ctx, inp.v_ctx)
+    anchors = np.asarray(inp.anchors).copy()
+    ctx = np.asarray(inp.ctx_lens).astype(np.int64).copy()
+    taps, offsets = inp.taps, np.asarray(inp.new_offsets)
+    P = w.block_size - 1
+    rec = {"drafts": [], "accepted": [], "bonus": [], "ctx_lens": []}
+    for s in range(steps):
+        append_context(w, W, k_cache, v_cache, taps, offsets, ctx)
+        fwd = draft_block(w, W, k_cache, v_cache, anchors, ctx)
+        zeta = fwd["zeta"]
+        ids, _ = topk(zeta.astype(np.float32).reshape(-1, w.vocab), w.top_k)
+        z = logit_transform(zeta, w.output_multiplier, w.final_logit_softcapping).astype(np.float32)
+        vals = np.take_along_axis(z.reshape(-1, w.vocab), ids.astype(np.int64), axis=1)
+        sel = select_path(anchors, ids.reshape(B, P, w.top_k), vals.reshape(B, P, w.top_k),
+                          W.sel_tl.data, W.sel_tr.data)
+        ver = verify_accept(sel["drafts"], target_logits_fn(s, sel["drafts"]))
+        rec["drafts"].append(sel["drafts"])
+        rec["accepted"].append(ver["accepted"])
+        rec["bonus"].append(ver["bonus"])
+        rec["ctx_lens"].append(ctx.copy())
+        n_new = ver["accepted"].astype(np.int64) + 1
+        taps, offsets = verified_taps_fn(ctx, n_new)
+        ctx = ctx + n_new
+        anchors = ver["bonus"].astype(np.int32)
+    return rec
+

@@ -47,6 +47,7 @@ class Workload:
     output_multiplier: float = 1.0
     final_logit_softcapping: float = 0.0
     sliding_window: int = 0
+    spare_context: int = 0           # extra cache rows for multi-step decoding
     weight_std: float = 0.02
     gain_jitter: float = 0.0     # norm gains = 1 + N(0, gain_jitter^2); 0 -> exactly 1
     selector_active: bool = False
@@ -73,8 +74,9 @@ class Workload:
     @property
     def max_context(self) -> int:
         # rows [ctx, ctx + block_size) hold the block's transient keys/values;
-        # rounded up to a multiple of 32 rows
-        return (self.ctx[1] + self.block_size + 31) // 32 * 32
+        # spare_context more rows let a decode loop grow the context; rounded
+        # up to a multiple of 32 rows
+        return (self.ctx[1] + self.spare_context + self.block_size + 31) // 32 * 32
 
     def abi_config(self) -> dict:
         """Field values of the C ABI's dflash2_config for this workload."""

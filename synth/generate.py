@@ -30,6 +30,7 @@ CHUNK = 1 << 22
 T_EMBED, T_LMHEAD, T_PROJ, T_PROJ_NORM, T_FINAL_NORM, T_SEL_L, T_SEL_R = range(7)
 L_CONV_ATTN, L_ATTN_NORM, L_WQKV, L_WO, L_CONV_FFN, L_FFN_NORM, L_WGU, L_WDOWN = range(8)
 S_ANCHOR, S_CTXLEN, S_ACCEPT, S_TAPS, S_KCACHE, S_VCACHE = range(1000, 1006)
+S_VERIFIED_TAPS = 1006
 V_LOGITS, V_PLANT = 2000, 2001
 X_SEL_IDS, X_SEL_VALS, X_SEL_ANCH = 3000, 3001, 3002
 
@@ -265,6 +266,26 @@ def make_step_inputs(w: Workload, seqs: Optional[np.ndarray] = None) -> StepInpu
         taps=encode(taps, w.act_dtype),
         k_ctx=k_ctx, v_ctx=v_ctx,
     )
+
+
+def make_verified_taps(w: Workload, starts: np.ndarray, counts: np.ndarray,
+                       seqs: Optional[np.ndarray] = None):
+    """Target hidden-state taps of newly verified positions, for a decode
+    loop: sequence seqs[i] gets rows for positions starts[i] ..
+    starts[i] + counts[i] - 1, each row N(0, 1) seeded by (sequence,
+    position), so a position's taps do not depend on which step verified it.
+    Returns (taps Tensor [sum(counts), num_taps, tap_width], offsets [B+1])."""
+    starts = np.asarray(starts, dtype=np.int64)
+    counts = np.asarray(counts, dtype=np.int64)
+    seqs = np.arange(len(starts)) if seqs is None else np.asarray(seqs)
+    offsets = np.zeros(len(starts) + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    taps = np.empty((int(offsets[-1]), w.num_taps, w.tap_width), dtype=np.float32)
+    for i, b in enumerate(seqs):
+        for j in range(int(counts[i])):
+            taps[offsets[i] + j] = normal((w.num_taps, w.tap_width),
+                                          (w.index, S_VERIFIED_TAPS, int(b), int(starts[i]) + j))
+    return encode(taps, w.act_dtype), offsets.astype(np.int32)
 
 
 def make_target_logits(w: Workload, drafts: np.ndarray, seqs: Optional[np.ndarray] = None,
