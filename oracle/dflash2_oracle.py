@@ -416,6 +416,250 @@ def verify_accept(drafts, target_logits) -> Dict[str, np.ndarray]:
 
 
 # ----------------------------------------------------------------------------
+# O8: draft length from the selector's transition confidence.
+# ----------------------------------------------------------------------------
+
+
+def path_confidence(anchors, cand_ids, cand_vals, path, tl, tr) -> np.ndarray:
+    """Confidence of each transition the chosen path takes.
+
+    [LC §Configuration Notes: a positive draft_p_min stops a path before a
+    low-confidence selector transition.]  Reading S6: at position t the
+    selector's local choice among the k candidates, given the predecessor the
+    path took (the anchor at t = 0), scores candidate j with the lattice's own
+    float32 transition score s_j = pi(c_prev, c_tj) + z_tj; the confidence is
+    the softmax of those k scores at the chosen candidate, evaluated here in
+    float64 on the float32 scores.  Returns conf [B, P] float64."""
+    cand_ids = np.asarray(cand_ids)
+    cand_vals = np.asarray(cand_vals, dtype=np.float32)
+    path = np.asarray(path)
+    B, P, k = cand_ids.shape
+    conf = np.empty((B, P), dtype=np.float64)
+    for b in range(B):
+        prev = int(anchors[b])
+        for t in range(P):
+            s = (pair_scores(tl, tr, [prev], cand_ids[b, t])[0] + cand_vals[b, t]).astype(np.float32)
+            s = s.astype(np.float64)
+            w = np.exp(s - s.max())
+            j = int(path[b, t])
+            conf[b, t] = w[j] / w.sum()
+            prev = int(cand_ids[b, t, j])
+    return conf
+
+
+def draft_lengths(conf, p_min: float, n_min: int = 0, n_max: Optional[int] = None) -> np.ndarray:
+    """Number of drafts proposed per sequence.
+
+    [LC §Configuration Notes: draft_p_min stops the path before a transition
+    whose confidence is below it; draft_n_max caps the draft length at
+    block_size - 1; LC §Complete Runnable Code: SpecConfig also carries
+    draft_n_min.]  Reading S7: n_max is clamped to [0, P] and n_min to
+    [0, n_max]; the path stops at the first position t >= n_min whose
+    confidence is below p_min (drafts 0..t-1 are proposed), else at P, and
+    never runs past n_max.  p_min = 0 never stops a path."""
+    conf = np.asarray(conf, dtype=np.float64)
+    B, P = conf.shape
+    hi = P if n_max is None else min(max(int(n_max), 0), P)
+    lo = min(max(int(n_min), 0), hi)
+    out = np.empty(B, dtype=np.int32)
+    for b in range(B):
+        n = P
+        for t in range(lo, P):
+            if conf[b, t] < p_min:
+                n = t
+                break
+        out[b] = min(n, hi)
+    return out
+
+
+def verify_accept_len(drafts, target_logits, draft_lens) -> Dict[str, np.ndarray]:
+    """Greedy verification of a path cut to draft_lens[b] drafts: the
+    accepted prefix stops at the length, and the bonus is the argmax of the
+    row after the last accepted draft (row draft_lens[b] when all are
+    accepted).  Same tie and -0.0 rules as verify_accept (Q23, Q27)."""
+    drafts = np.asarray(drafts)
+    z = canonical_f32(target_logits)
+    B, bs, V = z.shape
+    g = np.argmax(z, axis=2).astype(np.int32)
+    accepted = np.zeros(B, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n = 0
+        while n < int(draft_lens[b]) and g[b, n] == drafts[b, n]:
+            n += 1
+        accepted[b] = n
+        bonus[b] = g[b, n]
+    return {"accepted": accepted, "bonus": bonus, "argmax": g}
+
+
+# ----------------------------------------------------------------------------
+# O9: sampled (rejection) verification.
+# ----------------------------------------------------------------------------
+
+F32_MAX = float(np.finfo(np.float32).max)
+
+
+def clean_logits(z) -> np.ndarray:
+    """Reading S2: NaN -> -inf (probability 0), +inf -> the largest float32,
+    -0.0 -> +0.0; float32 inputs widened exactly to float64."""
+    x = np.asarray(z, dtype=np.float32).astype(np.float64)
+    x = np.where(np.isnan(x), -np.inf, x)
+    x = np.minimum(x, F32_MAX)
+    return x + 0.0
+
+
+def target_distribution(z_row, temperature: float, top_k: int = 0, top_p: float = 1.0) -> np.ndarray:
+    """The target's sampling distribution for one row of its logits, float64.
+
+    [AM §Key Config Fields, paragraph on spec_generate: temperature, top_p and
+    top_k truncate the target's own distribution, the one the drafts are
+    verified against; the DFlash 2 acceptance figures use temperature 1.0,
+    top-p 0.95, top-k 20.]  Readings:
+      S1  temperature 0 is greedy: a point mass on the row's argmax (ties to
+          the smallest id), the rule of the greedy verification;
+      S2  logits cleaned by clean_logits;
+      S3  weights e_v = exp((z_v - m) / T) with m the row maximum, and
+          e_v = 1 for every entry equal to m (so a row without a finite logit
+          is uniform over its entries);
+      S4  top-k (0 = off, >= V = off) keeps every entry whose value is at
+          least the k-th largest value counted with multiplicity, so an entry
+          tied with the k-th is kept;
+      S5  top-p (>= 1 = off) is applied after top-k: a kept entry stays when
+          the kept mass strictly above its value is below top_p times the
+          kept mass (the smallest prefix by value reaching top_p, with a
+          value group kept or dropped whole).
+    Returns p [V] summing to 1."""
+    z = clean_logits(z_row)
+    V = z.size
+    if temperature == 0:
+        zc = canonical_f32(np.asarray(z_row, dtype=np.float32)).astype(np.float64)
+        nan = np.isnan(zc)
+        g = 0
+        if not nan.all():
+            zz = np.where(nan, -np.inf, zc)
+            g = int(np.nonzero(~nan & (zz == zz[~nan].max()))[0][0])
+        p = np.zeros(V)
+        p[g] = 1.0
+        return p
+    m = z.max()
+    with np.errstate(invalid="ignore", over="ignore"):
+        e = np.exp((z - m) / temperature)
+    e[z == m] = 1.0
+    keep = np.ones(V, dtype=bool)
+    if 0 < top_k < V:
+        kth = np.sort(z)[::-1][top_k - 1]
+        keep &= z >= kth
+    if top_p < 1.0:
+        S = e[keep].sum()
+        above = np.zeros(V)
+        for g in np.unique(z[keep]):
+            above[z == g] = e[keep & (z > g)].sum()
+        keep &= above < top_p * S
+    p = np.where(keep, e, 0.0)
+    return p / p.sum()
+
+
+def inverse_cdf(p: np.ndarray, v: float) -> int:
+    """The smallest id j with sum_{i <= j} p_i > v, ids ascending (Reading
+    S8); no such j (only for v >= 1) gives the id of the largest p, ties to
+    the smallest id."""
+    c = np.cumsum(p)
+    hit = np.nonzero(c > v)[0]
+    return int(hit[0]) if hit.size else int(np.argmax(p))
+
+
+def verify_sample(drafts, target_logits, uniforms, temperature: float, top_k: int = 0,
+                  top_p: float = 1.0, draft_lens=None) -> Dict[str, np.ndarray]:
+    """Rejection-sampling verification of one deterministic draft path.
+
+    [AM §Key Config Fields: drafts are verified by rejection sampling against
+    the target's (truncated) distribution, so sampled decoding keeps the
+    target's output distribution; LC §Configuration Notes: the DFlash2 path
+    comes from the selector lattice, not from a vocabulary sampler.]  The
+    rule is speculative sampling (Leviathan, Kalman and Matias 2023; Chen et
+    al. 2023) with the draft distribution q_i a point mass on d_i
+    (Reading S9): draft i is accepted when u_i < min(1, p_i(d_i) / q_i(d_i))
+    = p_i(d_i); at the first rejection the bonus is drawn from max(p_i - q_i,
+    0) normalised (p_i with d_i struck out); when every proposed draft is
+    accepted the bonus is drawn from the next row's p.  Draws use
+    inverse_cdf with v = uniforms[b, bs-1].
+
+    uniforms [B, bs]: u_i for draft i in columns 0..bs-2, v in column bs-1.
+    draft_lens [B] (None = bs-1) cuts each path.
+    Returns accepted, bonus, draft_prob [B, bs-1] (p_i(d_i) for i below the
+    length, 0 beyond) and margin [B]: the smallest distance of any uniform
+    from the threshold it was compared with, and of the kept mass from the
+    top-p bound, for the decisions this sequence took."""
+    drafts = np.asarray(drafts)
+    z = np.asarray(target_logits, dtype=np.float32)
+    u = np.asarray(uniforms, dtype=np.float32).astype(np.float64)
+    assert np.all((u >= 0) & (u < 1)), "uniforms lie in [0, 1)"
+    exact = temperature == 0          # point masses: no rounding-sensitive decision
+    B, bs, V = z.shape
+    P = bs - 1
+    lens = np.full(B, P) if draft_lens is None else np.asarray(draft_lens)
+    accepted = np.zeros(B, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    draft_prob = np.zeros((B, P))
+    margin = np.full(B, np.inf)
+    for b in range(B):
+        n_len = int(lens[b])
+        n = 0
+        dist = None
+        while n <= n_len:
+            p = target_distribution(z[b, n], temperature, top_k, top_p)
+            margin[b] = min(margin[b], _top_p_margin(z[b, n], temperature, top_k, top_p))
+            if n == n_len:
+                dist = p
+                break
+            d = int(drafts[b, n])
+            q = np.zeros(V)
+            q[d] = 1.0
+            pd = p[d]
+            draft_prob[b, n] = pd
+            if not exact:
+                margin[b] = min(margin[b], abs(u[b, n] - min(1.0, pd / q[d])))
+            if u[b, n] < min(1.0, pd / q[d]):
+                n += 1
+                continue
+            r = np.maximum(p - q, 0.0)
+            dist = r / r.sum()
+            break
+        for i in range(n + 1, n_len):
+            p = target_distribution(z[b, i], temperature, top_k, top_p)
+            draft_prob[b, i] = p[int(drafts[b, i])]
+        accepted[b] = n
+        v = u[b, P]
+        bonus[b] = inverse_cdf(dist, v)
+        c = np.cumsum(dist)
+        j = int(bonus[b])
+        lo = c[j - 1] if j > 0 else 0.0
+        if not exact:
+            margin[b] = min(margin[b], abs(c[j] - v), abs(v - lo))
+    return {"accepted": accepted, "bonus": bonus, "draft_prob": draft_prob, "margin": margin}
+
+
+def _top_p_margin(z_row, temperature, top_k, top_p) -> float:
+    """Distance of the top-p decision nearest its bound, as a fraction of the
+    kept mass (inf when top-p is off or the temperature is 0)."""
+    if top_p >= 1.0 or temperature == 0:
+        return np.inf
+    z = clean_logits(z_row)
+    m = z.max()
+    with np.errstate(invalid="ignore", over="ignore"):
+        e = np.exp((z - m) / temperature)
+    e[z == m] = 1.0
+    keep = np.ones(z.size, dtype=bool)
+    if 0 < top_k < z.size:
+        keep &= z >= np.sort(z)[::-1][top_k - 1]
+    S = e[keep].sum()
+    vals = np.unique(z[keep])[::-1]
+    masses = np.array([e[keep & (z == g)].sum() for g in vals])
+    before = np.concatenate([[0.0], np.cumsum(masses)[:-1]]) / S
+    return float(np.min(np.abs(before - top_p)))
+
+
+# ----------------------------------------------------------------------------
 # The whole step.
 # ----------------------------------------------------------------------------
 
