@@ -41,7 +41,8 @@ class dflash2_weights(ctypes.Structure):
 
 
 KERNEL_KINDS = ("gemm", "lmhead_topk", "topk_merge", "norm", "qkv_epilogue", "kv_append", "swiglu",
-                "attention", "attn_combine", "select", "verify_partial", "verify_final")
+                "attention", "attn_combine", "select", "verify_partial", "verify_final", "sample_rows",
+                "sample_pick")
 
 
 class dflash2_trace_entry(ctypes.Structure):
@@ -69,7 +70,12 @@ def _load():
         "dflash2_draft_block": ([vp, vp, c_int32, i32p, vp, i32p, i32p, c_int64, vp, vp, i32p, f32p,
                                  f32p, f32p, vp, c_size_t], c_int32),
         "dflash2_select_path": ([vp, vp, c_int32, i32p, i32p, f32p, i32p, i32p, f32p, f32p], c_int32),
+        "dflash2_select_path_stop": ([vp, vp, c_int32, i32p, i32p, f32p, c_float, c_int32, c_int32, i32p, i32p,
+                                      i32p, f32p, f32p], c_int32),
         "dflash2_verify_workspace_size": ([c_int32, c_int32, c_int32, POINTER(c_size_t)], c_int32),
+        "dflash2_verify_sample_workspace_size": ([c_int32, c_int32, c_int32, POINTER(c_size_t)], c_int32),
+        "dflash2_verify_sample": ([vp, c_int32, c_int32, c_int32, i32p, i32p, f32p, f32p, c_float, c_int32,
+                                   c_float, i32p, i32p, f32p, vp, c_size_t], c_int32),
         "dflash2_verify_accept": ([vp, c_int32, c_int32, c_int32, i32p, f32p, i32p, i32p, i32p, vp,
                                    c_size_t], c_int32),
         "dflash2_trace_attach": ([POINTER(dflash2_trace_entry), c_int32], c_int32),
@@ -85,7 +91,8 @@ def _load():
 
 lib = _load()
 EXPORTED = ("dflash2_create", "dflash2_destroy", "dflash2_workspace_size", "dflash2_draft_block",
-            "dflash2_select_path", "dflash2_verify_workspace_size", "dflash2_verify_accept",
+            "dflash2_select_path", "dflash2_select_path_stop", "dflash2_verify_workspace_size",
+            "dflash2_verify_accept", "dflash2_verify_sample_workspace_size", "dflash2_verify_sample",
             "dflash2_trace_attach", "dflash2_trace_detach", "dflash2_last_error")
 
 
@@ -146,3 +153,24 @@ def dflash2_verify_accept(stream, batch, block_size, vocab, draft_tokens, target
                           bonus, target_argmax, workspace, workspace_bytes) -> None:
     _check(lib.dflash2_verify_accept(stream, batch, block_size, vocab, draft_tokens, target_logits,
                                      accepted, bonus, target_argmax, workspace, workspace_bytes))
+
+
+def dflash2_select_path_stop(handle, stream, batch, anchor_ids, topk_ids, topk_vals, p_min, n_min, n_max,
+                             path_idx, draft_tokens, draft_lens, path_conf, path_score) -> None:
+    _check(lib.dflash2_select_path_stop(handle, stream, batch, anchor_ids, topk_ids, topk_vals, float(p_min),
+                                        int(n_min), int(n_max), path_idx, draft_tokens, draft_lens, path_conf,
+                                        path_score))
+
+
+def dflash2_verify_sample_workspace_size(batch: int, block_size: int, vocab: int) -> int:
+    n = c_size_t()
+    _check(lib.dflash2_verify_sample_workspace_size(batch, block_size, vocab, ctypes.byref(n)))
+    return n.value
+
+
+def dflash2_verify_sample(stream, batch, block_size, vocab, draft_tokens, draft_lens, target_logits, uniforms,
+                          temperature, top_k, top_p, accepted, bonus, draft_prob, workspace,
+                          workspace_bytes) -> None:
+    _check(lib.dflash2_verify_sample(stream, batch, block_size, vocab, draft_tokens, draft_lens, target_logits,
+                                     uniforms, float(temperature), int(top_k), float(top_p), accepted, bonus,
+                                     draft_prob, workspace, workspace_bytes))

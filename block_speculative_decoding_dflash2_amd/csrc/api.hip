@@ -528,31 +528,65 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
   return ok();
 }
 
-dflash2_status dflash2_select_path(dflash2_handle* handle, hipStream_t stream, int32_t batch,
-                                   const int32_t* anchor_ids, const int32_t* topk_ids,
-                                   const float* topk_vals, int32_t* path_idx,
-                                   int32_t* draft_tokens, float* path_score, float* debug_pair) {
-  if (!handle) return fail(DFLASH2_ERR_INVALID_ARG, "select_path: null handle");
+}  // extern "C"
+
+namespace {
+dflash2_status select_impl(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                           const int32_t* anchor_ids, const int32_t* topk_ids, const float* topk_vals,
+                           int32_t* path_idx, int32_t* draft_tokens, float* path_score, float* debug_pair,
+                           float p_min, int32_t n_min, int32_t n_max, int32_t* draft_lens,
+                           float* path_conf, const char* name) {
+  if (!handle) return fail(DFLASH2_ERR_INVALID_ARG, "%s: null handle", name);
   const dflash2_config& c = handle->cfg;
   if (batch < 1 || batch > c.max_batch)
-    return fail(DFLASH2_ERR_SHAPE, "select_path: batch %d outside 1..max_batch %d", batch, c.max_batch);
+    return fail(DFLASH2_ERR_SHAPE, "%s: batch %d outside 1..max_batch %d", name, batch, c.max_batch);
   if (!anchor_ids || !topk_ids || !topk_vals || !path_idx || !draft_tokens)
-    return fail(DFLASH2_ERR_INVALID_ARG, "select_path: null pointer argument");
+    return fail(DFLASH2_ERR_INVALID_ARG, "%s: null pointer argument", name);
+  if (!(p_min >= 0.0f && p_min <= 1.0f))
+    return fail(DFLASH2_ERR_INVALID_ARG, "%s: p_min %g outside [0, 1]", name, double(p_min));
   SelectArgs a{};
   a.anchors = anchor_ids; a.ids = topk_ids; a.vals = topk_vals;
   a.tl = handle->w.sel_tl; a.tr = handle->w.sel_tr;
   a.B = batch; a.P = c.block_size - 1; a.k = c.selector_top_k; a.r = c.selector_rank; a.V = c.vocab;
   a.path = path_idx; a.drafts = draft_tokens; a.score = path_score; a.debug_pair = debug_pair;
+  a.p_min = p_min; a.n_min = n_min; a.n_max = n_max; a.lens = draft_lens; a.conf = path_conf;
   {
-    const int64_t pairs = int64_t(batch) * (int64_t(a.P - 1) * a.k * a.k + a.k);
+    const bool stop = draft_lens || path_conf;
+    const int64_t pairs = int64_t(batch) * (int64_t(a.P - 1) * a.k * a.k + a.k + (stop ? int64_t(a.P) * a.k : 0));
     const int64_t bytes = int64_t(batch) * a.P * a.k * 8 + int64_t(batch) * (a.P * a.k + 1) * 2 * a.r * 4 +
-                          int64_t(batch) * a.P * 8;
+                          int64_t(batch) * a.P * 8 + (stop ? int64_t(batch) * (a.P + 1) * 4 : 0);
     traced(stream, DFLASH2_K_SELECT, bytes, 2 * pairs * a.r,
            [&] { launch_select(a, select_window(a.k, a.r, a.P, kSelectLds), stream); });
   }
-  dflash2_status st = check_launch("select_path");
+  return check_launch(name);
+}
+}  // namespace
+
+extern "C" {
+
+dflash2_status dflash2_select_path(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                   const int32_t* anchor_ids, const int32_t* topk_ids,
+                                   const float* topk_vals, int32_t* path_idx,
+                                   int32_t* draft_tokens, float* path_score, float* debug_pair) {
+  const dflash2_status st = select_impl(handle, stream, batch, anchor_ids, topk_ids, topk_vals, path_idx,
+                                        draft_tokens, path_score, debug_pair, 0.0f, 0, 0, nullptr, nullptr,
+                                        "select_path");
   return st == DFLASH2_OK ? ok() : st;
 }
+
+dflash2_status dflash2_select_path_stop(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                        const int32_t* anchor_ids, const int32_t* topk_ids,
+                                        const float* topk_vals, float p_min, int32_t n_min,
+                                        int32_t n_max, int32_t* path_idx, int32_t* draft_tokens,
+                                        int32_t* draft_lens, float* path_conf, float* path_score) {
+  if (!draft_lens) return fail(DFLASH2_ERR_INVALID_ARG, "select_path_stop: null draft_lens");
+  const dflash2_status st = select_impl(handle, stream, batch, anchor_ids, topk_ids, topk_vals, path_idx,
+                                        draft_tokens, path_score, nullptr, p_min, n_min, n_max, draft_lens,
+                                        path_conf, "select_path_stop");
+  return st == DFLASH2_OK ? ok() : st;
+}
+
+}  // extern "C"
 
 namespace {
 struct VerifyPlan {
@@ -571,6 +605,8 @@ VerifyPlan plan_verify(int B, int bs, int V) {
 }
 }  // namespace
 
+extern "C" {
+
 dflash2_status dflash2_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
                                              size_t* bytes) {
   if (!bytes) return fail(DFLASH2_ERR_INVALID_ARG, "verify_workspace_size: null argument");
@@ -579,6 +615,37 @@ dflash2_status dflash2_verify_workspace_size(int32_t batch, int32_t block_size, 
   *bytes = plan_verify(batch, block_size, vocab).bytes;
   return ok();
 }
+
+}  // extern "C"
+
+namespace {
+dflash2_status greedy_impl(hipStream_t stream, int32_t batch, int32_t block_size, int32_t vocab,
+                           const int32_t* draft_tokens, const int32_t* draft_lens, const float* target_logits,
+                           int32_t* accepted, int32_t* bonus, int32_t* target_argmax, float* draft_prob,
+                           void* workspace, const char* name) {
+  const VerifyPlan vp = plan_verify(batch, block_size, vocab);
+  VerifyArgs a{};
+  a.drafts = draft_tokens; a.logits = target_logits;
+  a.B = batch; a.bs = block_size; a.V = vocab; a.nchunks = vp.nchunks; a.chunk = vp.chunk;
+  a.part = static_cast<uint64_t*>(workspace);
+  a.accepted = accepted; a.bonus = bonus; a.argmax = target_argmax;
+  a.lens = draft_lens; a.draft_prob = draft_prob;
+  traced(stream, DFLASH2_K_VERIFY_PARTIAL, int64_t(batch) * block_size * vocab * 4, 0,
+         [&] { launch_verify_partial(a, stream); });
+  traced(stream, DFLASH2_K_VERIFY_FINAL, int64_t(batch) * (block_size - 1) * 4 + int64_t(batch) * 8, 0,
+         [&] { launch_verify_final(a, stream); });
+  return check_launch(name);
+}
+
+// Row results of the sampled verification: theta, max key [rows] u32; kept
+// mass S, draft weight Ed [rows] u64.
+size_t sample_ws_bytes(int B, int bs) {
+  const size_t rows = size_t(B) * bs;
+  return align_up(rows * 4) * 2 + align_up(rows * 8) * 2;
+}
+}  // namespace
+
+extern "C" {
 
 dflash2_status dflash2_verify_accept(hipStream_t stream, int32_t batch, int32_t block_size,
                                      int32_t vocab, const int32_t* draft_tokens,
@@ -593,16 +660,68 @@ dflash2_status dflash2_verify_accept(hipStream_t stream, int32_t batch, int32_t 
   const VerifyPlan vp = plan_verify(batch, block_size, vocab);
   if (!workspace || workspace_bytes < vp.bytes || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
     return fail(DFLASH2_ERR_WORKSPACE, "verify_accept: workspace needs %zu bytes, 256-aligned", vp.bytes);
-  VerifyArgs a{};
-  a.drafts = draft_tokens; a.logits = target_logits;
-  a.B = batch; a.bs = block_size; a.V = vocab; a.nchunks = vp.nchunks; a.chunk = vp.chunk;
-  a.part = static_cast<uint64_t*>(workspace);
-  a.accepted = accepted; a.bonus = bonus; a.argmax = target_argmax;
-  traced(stream, DFLASH2_K_VERIFY_PARTIAL, int64_t(batch) * block_size * vocab * 4, 0,
-         [&] { launch_verify_partial(a, stream); });
-  traced(stream, DFLASH2_K_VERIFY_FINAL, int64_t(batch) * (block_size - 1) * 4 + int64_t(batch) * 8, 0,
-         [&] { launch_verify_final(a, stream); });
-  dflash2_status st = check_launch("verify_accept");
+  const dflash2_status st = greedy_impl(stream, batch, block_size, vocab, draft_tokens, nullptr, target_logits,
+                                        accepted, bonus, target_argmax, nullptr, workspace, "verify_accept");
+  return st == DFLASH2_OK ? ok() : st;
+}
+
+dflash2_status dflash2_verify_sample_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
+                                                    size_t* bytes) {
+  if (!bytes) return fail(DFLASH2_ERR_INVALID_ARG, "verify_sample_workspace_size: null argument");
+  if (batch < 1 || block_size < 2 || vocab < 1)
+    return fail(DFLASH2_ERR_SHAPE, "verify_sample_workspace_size: bad sizes");
+  *bytes = std::max(plan_verify(batch, block_size, vocab).bytes, sample_ws_bytes(batch, block_size));
+  return ok();
+}
+
+dflash2_status dflash2_verify_sample(hipStream_t stream, int32_t batch, int32_t block_size, int32_t vocab,
+                                     const int32_t* draft_tokens, const int32_t* draft_lens,
+                                     const float* target_logits, const float* uniforms, float temperature,
+                                     int32_t top_k, float top_p, int32_t* accepted, int32_t* bonus,
+                                     float* draft_prob, void* workspace, size_t workspace_bytes) {
+  if (batch < 1 || block_size < 2 || vocab < 1)
+    return fail(DFLASH2_ERR_SHAPE, "verify_sample: bad sizes (batch %d, block_size %d, vocab %d)",
+                batch, block_size, vocab);
+  if (!draft_tokens || !target_logits || !accepted || !bonus)
+    return fail(DFLASH2_ERR_INVALID_ARG, "verify_sample: null pointer argument");
+  if (!(temperature >= 0.0f) || std::isinf(temperature))
+    return fail(DFLASH2_ERR_INVALID_ARG, "verify_sample: temperature %g is not finite and >= 0",
+                double(temperature));
+  if (top_k < 0) return fail(DFLASH2_ERR_INVALID_ARG, "verify_sample: top_k %d < 0", top_k);
+  if (!(top_p > 0.0f)) return fail(DFLASH2_ERR_INVALID_ARG, "verify_sample: top_p %g is not > 0", double(top_p));
+  if (temperature > 0.0f && !uniforms)
+    return fail(DFLASH2_ERR_INVALID_ARG, "verify_sample: null uniforms with temperature > 0");
+  size_t need = 0;
+  dflash2_verify_sample_workspace_size(batch, block_size, vocab, &need);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return fail(DFLASH2_ERR_WORKSPACE, "verify_sample: workspace needs %zu bytes, 256-aligned", need);
+  dflash2_status st;
+  if (temperature == 0.0f) {
+    st = greedy_impl(stream, batch, block_size, vocab, draft_tokens, draft_lens, target_logits, accepted, bonus,
+                     nullptr, draft_prob, workspace, "verify_sample");
+  } else {
+    int bits = 0;
+    while ((int64_t(1) << bits) < int64_t(vocab)) ++bits;
+    const size_t rows = size_t(batch) * block_size;
+    char* ws = static_cast<char*>(workspace);
+    SampleArgs a{};
+    a.logits = target_logits; a.drafts = draft_tokens; a.lens = draft_lens; a.uni = uniforms;
+    a.temp = temperature;
+    a.top_k = (top_k >= vocab) ? 0 : top_k;
+    a.top_p = top_p >= 1.0f ? 1.0f : top_p;
+    a.qscale = std::ldexp(1.0f, 52 - bits);
+    a.B = batch; a.bs = block_size; a.V = vocab;
+    a.theta = reinterpret_cast<uint32_t*>(ws);
+    a.mkey = reinterpret_cast<uint32_t*>(ws + align_up(rows * 4));
+    a.S = reinterpret_cast<uint64_t*>(ws + 2 * align_up(rows * 4));
+    a.Ed = reinterpret_cast<uint64_t*>(ws + 2 * align_up(rows * 4) + align_up(rows * 8));
+    a.accepted = accepted; a.bonus = bonus; a.draft_prob = draft_prob;
+    traced(stream, DFLASH2_K_SAMPLE_ROWS, int64_t(rows) * vocab * 4 + int64_t(rows) * 24, 0,
+           [&] { launch_sample_rows(a, stream); });
+    traced(stream, DFLASH2_K_SAMPLE_PICK, int64_t(batch) * vocab * 4 + int64_t(rows) * 28, 0,
+           [&] { launch_sample_pick(a, stream); });
+    st = check_launch("verify_sample");
+  }
   return st == DFLASH2_OK ? ok() : st;
 }
 

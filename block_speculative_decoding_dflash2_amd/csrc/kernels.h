@@ -137,6 +137,10 @@ struct SelectArgs {
   const float* tl; const float* tr;
   int B, P, k, r, V;
   int32_t* path; int32_t* drafts; float* score; float* debug_pair;
+  // transition confidence along the path and the draft-length rule
+  // (computed when lens or conf is non-null)
+  float p_min; int n_min, n_max;
+  int32_t* lens; float* conf;
 };
 
 struct VerifyArgs {
@@ -144,6 +148,16 @@ struct VerifyArgs {
   int B, bs, V, nchunks, chunk;
   uint64_t* part;                 // [B*bs][nchunks]
   int32_t* accepted; int32_t* bonus; int32_t* argmax;
+  const int32_t* lens;            // [B] draft lengths, nullable (= bs-1)
+  float* draft_prob;              // [B][bs-1] nullable: 1 where the draft is the argmax
+};
+
+struct SampleArgs {
+  const float* logits; const int32_t* drafts; const int32_t* lens; const float* uni;
+  float temp; int top_k; float top_p; float qscale;   // top_k 0 = off, top_p >= 1 = off
+  int B, bs, V;
+  uint32_t* theta; uint32_t* mkey; uint64_t* S; uint64_t* Ed;   // [B*bs] row results
+  int32_t* accepted; int32_t* bonus; float* draft_prob;
 };
 
 // Activation rows above which the LDS-tiled, compute-bound GEMMs are used.
@@ -175,6 +189,8 @@ __host__ __device__ int select_row_stride(int r);
 int select_window(int k, int r, int P, size_t budget);
 void launch_select(const SelectArgs& a, int tw, hipStream_t s);
 void launch_verify_partial(const VerifyArgs& a, hipStream_t s);
+void launch_sample_rows(const SampleArgs& a, hipStream_t s);
+void launch_sample_pick(const SampleArgs& a, hipStream_t s);
 void launch_verify_final(const VerifyArgs& a, hipStream_t s);
 
 }  // namespace dfl

@@ -65,7 +65,7 @@ __host__ __device__ int select_row_stride(int r) { return (r + 3) / 4 * 4 + 4; }
 // j = candidate j; lanes of one wave run in lockstep, so S is read for every
 // i before any lane overwrites it).
 // LDS: TL [tw*k][RS], TR [tw*k][RS], PAIR [tw][k][k], S [k], BACK [P][k],
-// PATH [P], TOK [2*tw*k], VAL [tw*k].
+// PATH [P], TOK [2*tw*k], VAL [tw*k], CONF [P].
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int b = blockIdx.x;
@@ -239,18 +239,61 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
     p.path[int64_t(b) * P + t] = j;
     p.drafts[int64_t(b) * P + t] = ids[t * k + j];
   }
+  if (!p.lens && !p.conf) return;
+  // ---- confidence of each transition the path takes (llama-cpp-python
+  // wiki, "Configuration Notes": draft_p_min stops a path before a
+  // low-confidence selector transition): softmax over the k candidates of
+  // the lattice's own float32 scores pi(c_prev, c_j) + z_j, c_prev = the
+  // predecessor the path took.  One wave per position, lane j = candidate j;
+  // pi is summed in the selector's order (multiply, then add, m ascending).
+  float* CONF = VAL + tw * k;  // [P]
+  const int wave = tid / WAVE, lane = tid & (WAVE - 1);
+  for (int t = wave; t < P; t += 256 / WAVE) {
+    const int prev = t == 0 ? anchor : ids[(t - 1) * k + PATH[t - 1]];
+    float sj = -INFINITY;
+    if (lane < k) {
+      const int cj = ids[t * k + lane];
+      const bool okp = prev >= 0 && prev < V, okc = cj >= 0 && cj < V;
+      float acc = 0.0f;
+      for (int m = 0; m < r; ++m) {
+        const float a = okp ? p.tl[int64_t(prev) * r + m] : 0.0f;
+        const float c = okc ? p.tr[int64_t(cj) * r + m] : 0.0f;
+        const float prod = a * c;
+        acc = acc + prod;
+      }
+      sj = acc + vals[t * k + lane];
+    }
+    const float mx = wave_max(sj);
+    const float e = lane < k ? expf(sj - mx) : 0.0f;
+    const float den = wave_sum(e);
+    const float mine = __shfl(e, PATH[t], WAVE);
+    if (lane == 0) {
+      const float cf = mine / den;
+      CONF[t] = cf;
+      if (p.conf) p.conf[int64_t(b) * P + t] = cf;
+    }
+  }
+  __syncthreads();
+  if (p.lens && tid == 0) {
+    const int hi = min(max(p.n_max, 0), P);
+    const int lo = min(max(p.n_min, 0), hi);
+    int n = P;
+    for (int t = lo; t < P; ++t)
+      if (CONF[t] < p.p_min) { n = t; break; }
+    p.lens[b] = min(n, hi);
+  }
 }
 
 // Transitions per window that fit the LDS budget (0: does not fit).
 int select_window(int k, int r, int P, size_t budget) {
   const size_t per = size_t(2 * k * select_row_stride(r) + k * k + 3 * k) * 4;
-  const size_t fixed = size_t(k + P * k + P) * 4;
+  const size_t fixed = size_t(k + P * k + 2 * P) * 4;
   if (fixed + per > budget) return 0;
   return int(std::min<size_t>(size_t(P), (budget - fixed) / per));
 }
 
 static size_t select_lds_bytes(int k, int r, int P, int tw) {
-  return size_t(2 * tw * k * select_row_stride(r) + tw * k * k + k + P * k + P + 3 * tw * k) * 4;
+  return size_t(2 * tw * k * select_row_stride(r) + tw * k * k + k + P * k + 2 * P + 3 * tw * k) * 4;
 }
 
 void launch_select(const SelectArgs& a, int tw, hipStream_t s) {
@@ -310,13 +353,17 @@ __global__ __launch_bounds__(256) void verify_final_kernel(VerifyArgs p) {
     }
   }
   __syncthreads();
+  const int P = p.bs - 1;
+  const int len = p.lens ? min(max(p.lens[b], 0), P) : P;
   if (threadIdx.x == 0) {
-    const int P = p.bs - 1;
     int n = 0;
-    while (n < P && gl[n] == p.drafts[int64_t(b) * P + n]) ++n;
+    while (n < len && gl[n] == p.drafts[int64_t(b) * P + n]) ++n;
     p.accepted[b] = n;
     p.bonus[b] = gl[n];
   }
+  if (p.draft_prob)
+    for (int i = threadIdx.x; i < P; i += blockDim.x)
+      p.draft_prob[int64_t(b) * P + i] = (i < len && gl[i] == p.drafts[int64_t(b) * P + i]) ? 1.0f : 0.0f;
 }
 
 void launch_verify_partial(const VerifyArgs& a, hipStream_t s) {

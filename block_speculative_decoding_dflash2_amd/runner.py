@@ -162,6 +162,28 @@ class DFlash2:
                               ptr(draft_tokens), ptr(score), ptr(pair))
         return {"path": path_idx, "drafts": draft_tokens, "score": score, "pair": pair}
 
+    def select_path_stop(self, anchors, topk_ids, topk_vals, p_min=0.0, n_min=0, n_max=None,
+                         want_conf=False, want_score=False, path_idx=None, draft_tokens=None,
+                         draft_lens=None, stream=None):
+        """select_path plus the draft-length rule (draft_p_min / n_min / n_max)."""
+        c = self.cfg
+        B = anchors.numel()
+        P = c["block_size"] - 1
+        dev = self.device
+        if path_idx is None:
+            path_idx = torch.empty((B, P), dtype=torch.int32, device=dev)
+        if draft_tokens is None:
+            draft_tokens = torch.empty((B, P), dtype=torch.int32, device=dev)
+        if draft_lens is None:
+            draft_lens = torch.empty((B,), dtype=torch.int32, device=dev)
+        conf = torch.empty((B, P), dtype=torch.float32, device=dev) if want_conf else None
+        score = torch.empty((B,), dtype=torch.float32, device=dev) if want_score else None
+        L.dflash2_select_path_stop(self.handle, current_stream() if stream is None else stream, B,
+                                   ptr(anchors), ptr(topk_ids), ptr(topk_vals), p_min, n_min,
+                                   P if n_max is None else n_max, ptr(path_idx), ptr(draft_tokens),
+                                   ptr(draft_lens), ptr(conf), ptr(score))
+        return {"path": path_idx, "drafts": draft_tokens, "lens": draft_lens, "conf": conf, "score": score}
+
 
 class KernelTrace:
     """Per-kernel HIP-event timing of every library launch made on this
@@ -230,3 +252,27 @@ def verify_accept(draft_tokens, target_logits, want_argmax=False, workspace=None
                             ptr(draft_tokens), ptr(target_logits), ptr(accepted), ptr(bonus), ptr(am),
                             ptr(workspace), workspace.numel())
     return {"accepted": accepted, "bonus": bonus, "argmax": am}
+
+
+def verify_sample_workspace(batch: int, block_size: int, vocab: int, device="cuda") -> torch.Tensor:
+    n = L.dflash2_verify_sample_workspace_size(batch, block_size, vocab)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def verify_sample(draft_tokens, target_logits, uniforms, temperature, top_k=0, top_p=1.0, draft_lens=None,
+                  want_prob=False, workspace=None, accepted=None, bonus=None, stream=None):
+    """Rejection-sampling verification (dflash2_verify_sample).  uniforms
+    [B, bs] float32 on the device: u_i in columns 0..bs-2, the draw's v last."""
+    B, bs, V = target_logits.shape
+    dev = target_logits.device
+    if accepted is None:
+        accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    prob = torch.empty((B, bs - 1), dtype=torch.float32, device=dev) if want_prob else None
+    if workspace is None:
+        workspace = verify_sample_workspace(B, bs, V, dev)
+    L.dflash2_verify_sample(current_stream() if stream is None else stream, B, bs, V, ptr(draft_tokens),
+                            ptr(draft_lens), ptr(target_logits), ptr(uniforms), temperature, top_k, top_p,
+                            ptr(accepted), ptr(bonus), ptr(prob), ptr(workspace), workspace.numel())
+    return {"accepted": accepted, "bonus": bonus, "draft_prob": prob}

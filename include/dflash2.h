@@ -214,6 +214,29 @@ dflash2_status dflash2_select_path(dflash2_handle* handle, hipStream_t stream, i
                                    const float* topk_vals, int32_t* path_idx,
                                    int32_t* draft_tokens, float* path_score, float* debug_pair);
 
+/* Step 4 with the draft-length rule (llama-cpp-python wiki, "DFlash2
+ * Speculative Decoding", "Configuration Notes": a positive draft_p_min stops
+ * a path before a low-confidence selector transition; draft_n_max caps the
+ * draft at block_size-1; "Complete Runnable Code": SpecConfig also carries
+ * draft_n_min).  The path, drafts and score are exactly those of
+ * dflash2_select_path.  Then, per position t, the transition's confidence is
+ * the softmax over the k candidates of the lattice's float32 scores
+ * pi(c_prev, c_j) + topk_vals[b, t, j], c_prev being the predecessor the path
+ * took (the anchor at t = 0), taken at the chosen candidate (float32 expf).
+ * draft_lens[b] = min(n_max', first t >= n_min' with conf < p_min, else
+ * block_size-1), where n_max' = n_max clamped to [0, block_size-1] and
+ * n_min' = n_min clamped to [0, n_max'].  p_min = 0 never stops a path.
+ *   p_min      in [0, 1], else DFLASH2_ERR_INVALID_ARG.
+ *   draft_lens [device] int32 [batch] (required).
+ *   path_conf  [device, nullable] float [batch, block_size-1].
+ *   path_score [device, nullable] float [batch].
+ * No workspace; 1 <= batch <= max_batch. */
+dflash2_status dflash2_select_path_stop(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                        const int32_t* anchor_ids, const int32_t* topk_ids,
+                                        const float* topk_vals, float p_min, int32_t n_min,
+                                        int32_t n_max, int32_t* path_idx, int32_t* draft_tokens,
+                                        int32_t* draft_lens, float* path_conf, float* path_score);
+
 /* Bytes of device workspace dflash2_verify_accept needs. */
 dflash2_status dflash2_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
                                              size_t* bytes);
@@ -233,6 +256,51 @@ dflash2_status dflash2_verify_accept(hipStream_t stream, int32_t batch, int32_t 
                                      const float* target_logits, int32_t* accepted,
                                      int32_t* bonus, int32_t* target_argmax, void* workspace,
                                      size_t workspace_bytes);
+
+/* Bytes of device workspace dflash2_verify_sample needs (>= the greedy
+ * verification's). */
+dflash2_status dflash2_verify_sample_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
+                                                    size_t* bytes);
+
+/* Step 5 with sampling, stateless (NeMo AutoModel page, "Key Config Fields",
+ * paragraph on spec_generate: temperature, top-p and top-k truncate the
+ * target's distribution and rejection sampling verifies the drafts against
+ * it, so sampled decoding keeps the target's output distribution).  Row i of
+ * target_logits [device] float [batch, block_size, vocab] is the target's
+ * prediction after block slot i.  Per row the target distribution is
+ *   p_v = e_v / S over the kept set,  e_v = exp((z_v - m) / temperature),
+ * m = the row maximum; NaN logits weigh 0, +inf acts as FLT_MAX, entries
+ * equal to m weigh 1.  The kept set: top_k (0 or >= vocab: off) keeps every
+ * entry >= the top_k-th largest value (ties kept); then top_p (>= 1: off)
+ * keeps an entry while the kept mass strictly above its value is below
+ * top_p times the kept mass (equal values kept or dropped together).
+ * The draft path is deterministic (a point mass on each draft), so draft i
+ * (i < draft_lens[b]) is accepted while u_i < p_i(d_i); at the first
+ * rejection the bonus is drawn from p_i with d_i struck out; when every
+ * proposed draft is accepted it is drawn from row draft_lens[b].  A draw is
+ * the smallest id j (ascending ids) whose cumulative mass exceeds v * total.
+ * Weights are 64-bit fixed point (e_v * 2^(52 - ceil(log2 vocab)), rounded),
+ * so all sums and decisions are exact and deterministic; they differ from
+ * real arithmetic by at most vocab * 2^-(53 - ceil(log2 vocab)) of the mass.
+ * temperature 0 is the greedy rule of dflash2_verify_accept (uniforms unused).
+ *   draft_tokens [device] int32 [batch, block_size-1]
+ *   draft_lens   [device, nullable] int32 [batch]: drafts proposed per
+ *                sequence, clamped to [0, block_size-1]; null = all.
+ *   uniforms     [device] float [batch, block_size] in [0, 1): column i
+ *                (< block_size-1) is u_i, the last column is v (a value
+ *                outside [0, 1) gives some token of the row, unspecified).
+ *   temperature  finite, >= 0; top_k >= 0; top_p > 0; else
+ *                DFLASH2_ERR_INVALID_ARG.
+ *   accepted, bonus [device] int32 [batch]
+ *   draft_prob   [device, nullable] float [batch, block_size-1]: p_i(d_i)
+ *                for i < draft_lens[b], 0 beyond.
+ *   workspace    [device] >= dflash2_verify_sample_workspace_size bytes,
+ *                256-aligned. */
+dflash2_status dflash2_verify_sample(hipStream_t stream, int32_t batch, int32_t block_size, int32_t vocab,
+                                     const int32_t* draft_tokens, const int32_t* draft_lens,
+                                     const float* target_logits, const float* uniforms, float temperature,
+                                     int32_t top_k, float top_p, int32_t* accepted, int32_t* bonus,
+                                     float* draft_prob, void* workspace, size_t workspace_bytes);
 
 /* Optional per-kernel timing (instrumentation for benchmarks and profiling).
  * While a trace is attached on a thread, every kernel that calls from this
@@ -256,7 +324,9 @@ typedef enum {
   DFLASH2_K_ATTN_COMBINE = 8,
   DFLASH2_K_SELECT = 9,
   DFLASH2_K_VERIFY_PARTIAL = 10,
-  DFLASH2_K_VERIFY_FINAL = 11
+  DFLASH2_K_VERIFY_FINAL = 11,
+  DFLASH2_K_SAMPLE_ROWS = 12,  /* sampled verification: per-row truncation */
+  DFLASH2_K_SAMPLE_PICK = 13   /* sampled verification: accept walk + draw */
 } dflash2_kernel_kind;
 
 typedef struct {

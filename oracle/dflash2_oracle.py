@@ -541,22 +541,64 @@ def target_distribution(z_row, temperature: float, top_k: int = 0, top_p: float 
         p = np.zeros(V)
         p[g] = 1.0
         return p
+    e, keep = _weights_top_k(z, temperature, top_k)
+    if top_p < 1.0:
+        S = e[keep].sum()
+        above = _mass_strictly_above(z, e, keep)
+        keep &= above < top_p * S
+    p = np.where(keep, e, 0.0)
+    return p / p.sum()
+
+
+def _weights_top_k(z, temperature, top_k):
+    """Readings S3 and S4 on cleaned logits: weights and the top-k kept mask."""
     m = z.max()
     with np.errstate(invalid="ignore", over="ignore"):
         e = np.exp((z - m) / temperature)
     e[z == m] = 1.0
-    keep = np.ones(V, dtype=bool)
-    if 0 < top_k < V:
+    keep = np.ones(z.size, dtype=bool)
+    if 0 < top_k < z.size:
         kth = np.sort(z)[::-1][top_k - 1]
         keep &= z >= kth
-    if top_p < 1.0:
-        S = e[keep].sum()
-        above = np.zeros(V)
-        for g in np.unique(z[keep]):
-            above[z == g] = e[keep & (z > g)].sum()
-        keep &= above < top_p * S
-    p = np.where(keep, e, 0.0)
-    return p / p.sum()
+    return e, keep
+
+
+def target_distributions_near(z_row, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                              band: float = 0.0) -> list:
+    """Every distribution target_distribution would give if the top-p bound
+    were moved anywhere within [top_p - band, top_p + band] (a value group
+    whose kept mass above lies that close to the bound may be kept or
+    dropped by an evaluation with rounding error below band).  The first
+    entry is target_distribution itself."""
+    exact = target_distribution(z_row, temperature, top_k, top_p)
+    if temperature == 0 or top_p >= 1.0 or band <= 0:
+        return [exact]
+    z = clean_logits(z_row)
+    e, keep = _weights_top_k(z, temperature, top_k)
+    S = e[keep].sum()
+    frac = _mass_strictly_above(z, e, keep) / S
+    out, seen = [exact], {int(np.count_nonzero(exact))}
+    levels = np.unique(frac[keep])
+    cuts = [top_p - band] + [float(np.nextafter(L, 2.0)) for L in levels if top_p - band < L <= top_p + band]
+    for c in cuts:
+        kp = keep & (frac < c)
+        if not kp.any() or int(np.count_nonzero(kp)) in seen:
+            continue
+        seen.add(int(np.count_nonzero(kp)))
+        q = np.where(kp, e, 0.0)
+        out.append(q / q.sum())
+    return out
+
+
+def _mass_strictly_above(z, e, keep) -> np.ndarray:
+    """For every kept entry, the kept mass of strictly larger values (value
+    groups summed with np.unique, then accumulated from the top)."""
+    vals, inv = np.unique(z[keep], return_inverse=True)       # ascending
+    group_mass = np.bincount(inv, weights=e[keep], minlength=vals.size)
+    above_group = np.cumsum(group_mass[::-1])[::-1] - group_mass   # larger values only
+    above = np.zeros(z.size)
+    above[keep] = above_group[inv]
+    return above
 
 
 def inverse_cdf(p: np.ndarray, v: float) -> int:
@@ -588,8 +630,8 @@ def verify_sample(drafts, target_logits, uniforms, temperature: float, top_k: in
     draft_lens [B] (None = bs-1) cuts each path.
     Returns accepted, bonus, draft_prob [B, bs-1] (p_i(d_i) for i below the
     length, 0 beyond) and margin [B]: the smallest distance of any uniform
-    from the threshold it was compared with, and of the kept mass from the
-    top-p bound, for the decisions this sequence took."""
+    from the threshold it was compared with, for the decisions this sequence
+    took (target_distributions_near covers the top-p bound)."""
     drafts = np.asarray(drafts)
     z = np.asarray(target_logits, dtype=np.float32)
     u = np.asarray(uniforms, dtype=np.float32).astype(np.float64)
@@ -608,7 +650,6 @@ def verify_sample(drafts, target_logits, uniforms, temperature: float, top_k: in
         dist = None
         while n <= n_len:
             p = target_distribution(z[b, n], temperature, top_k, top_p)
-            margin[b] = min(margin[b], _top_p_margin(z[b, n], temperature, top_k, top_p))
             if n == n_len:
                 dist = p
                 break
@@ -639,23 +680,15 @@ def verify_sample(drafts, target_logits, uniforms, temperature: float, top_k: in
     return {"accepted": accepted, "bonus": bonus, "draft_prob": draft_prob, "margin": margin}
 
 
-def _top_p_margin(z_row, temperature, top_k, top_p) -> float:
+def top_p_margin(z_row, temperature, top_k, top_p) -> float:
     """Distance of the top-p decision nearest its bound, as a fraction of the
     kept mass (inf when top-p is off or the temperature is 0)."""
     if top_p >= 1.0 or temperature == 0:
         return np.inf
     z = clean_logits(z_row)
-    m = z.max()
-    with np.errstate(invalid="ignore", over="ignore"):
-        e = np.exp((z - m) / temperature)
-    e[z == m] = 1.0
-    keep = np.ones(z.size, dtype=bool)
-    if 0 < top_k < z.size:
-        keep &= z >= np.sort(z)[::-1][top_k - 1]
+    e, keep = _weights_top_k(z, temperature, top_k)
     S = e[keep].sum()
-    vals = np.unique(z[keep])[::-1]
-    masses = np.array([e[keep & (z == g)].sum() for g in vals])
-    before = np.concatenate([[0.0], np.cumsum(masses)[:-1]]) / S
+    before = _mass_strictly_above(z, e, keep)[keep] / S
     return float(np.min(np.abs(before - top_p)))
 
 

@@ -32,6 +32,7 @@ L_CONV_ATTN, L_ATTN_NORM, L_WQKV, L_WO, L_CONV_FFN, L_FFN_NORM, L_WGU, L_WDOWN =
 S_ANCHOR, S_CTXLEN, S_ACCEPT, S_TAPS, S_KCACHE, S_VCACHE = range(1000, 1006)
 S_VERIFIED_TAPS = 1006
 V_LOGITS, V_PLANT = 2000, 2001
+V_SAMPLE_LOGITS, V_SAMPLE_PLANT, V_UNIFORM = 2002, 2003, 2004
 X_SEL_IDS, X_SEL_VALS, X_SEL_ANCH = 3000, 3001, 3002
 
 
@@ -323,6 +324,41 @@ def make_target_logits(w: Workload, drafts: np.ndarray, seqs: Optional[np.ndarra
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(work, range(len(seqs))))
     return out
+
+
+def make_sampling_inputs(B: int, bs: int, V: int, tag: int = 0, spread: float = 2.0, boost: float = 16.0,
+                         agree: float = 0.8, quantum: float = 0.0):
+    """Inputs of sampled verification: drafts [B, bs-1] uniform over the
+    vocabulary and target logits [B, bs, V] float32 N(0, spread^2), where the
+    draft's logit in row i < bs-1 is raised with probability `agree` by
+    boost * U(0.3, 1) (from an unlikely to an almost certain token of the
+    target).  quantum > 0 rounds every logit to a multiple of it, so equal
+    values are common."""
+    drng = np.random.default_rng([SEED, V_SAMPLE_PLANT, tag, B, bs, V])
+    drafts = drng.integers(0, V, size=(B, bs - 1)).astype(np.int32)
+    raise_it = drng.random((B, bs - 1)) < agree
+    amount = (boost * drng.uniform(0.3, 1.0, size=(B, bs - 1))).astype(np.float32)
+    out = np.empty((B, bs, V), dtype=np.float32)
+
+    def work(b):
+        rows = normal((bs, V), (V_SAMPLE_LOGITS, tag, b, V), std=spread)
+        for r in range(bs - 1):
+            if raise_it[b, r]:
+                rows[r, drafts[b, r]] += amount[b, r]
+        if quantum > 0:
+            rows = (np.round(rows / np.float32(quantum)) * np.float32(quantum)).astype(np.float32)
+        out[b] = rows
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(B)))
+    return drafts, out
+
+
+def make_uniforms(shape, tag: int = 0) -> np.ndarray:
+    """float32 uniforms k / 2^24, k uniform on 0 .. 2^24 - 1: exact in
+    float32 and strictly below 1."""
+    rng = np.random.default_rng([SEED, V_UNIFORM, tag, *[int(x) for x in shape]])
+    return (rng.integers(0, 1 << 24, size=shape) / float(1 << 24)).astype(np.float32)
 
 
 def make_selector_inputs(w: Workload, tag: int = 0, integer_lattice: bool = False) -> Dict[str, np.ndarray]:

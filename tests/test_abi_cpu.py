@@ -140,6 +140,17 @@ def test_workspace_size_and_draft_argument_errors():
         with pytest.raises(L.DFlash2Error) as e:
             L.dflash2_select_path(h, None, 3, p, p, p, p, p, None, None)
         assert e.value.status == L.DFLASH2_ERR_SHAPE
+        # the stop variant: lengths are required, p_min lies in [0, 1]
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_select_path_stop(h, None, 1, p, p, p, 0.1, 0, 7, p, p, None, None, None)
+        assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
+        for bad in (-0.1, 1.5, float("nan")):
+            with pytest.raises(L.DFlash2Error) as e:
+                L.dflash2_select_path_stop(h, None, 1, p, p, p, bad, 0, 7, p, p, p, None, None)
+            assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_select_path_stop(h, None, 3, p, p, p, 0.1, 0, 7, p, p, p, None, None)
+        assert e.value.status == L.DFLASH2_ERR_SHAPE
     finally:
         L.dflash2_destroy(h)
 
@@ -173,3 +184,30 @@ def test_speculative_metrics_fixture():
     m = pkg.metrics.speculative_metrics(g["per_step_accepted"], g["num_spec_tokens"])
     for k, v in g["expected"].items():
         assert m[k] == pytest.approx(v) if isinstance(v, float) else m[k] == v, k
+
+
+def test_verify_sample_argument_errors():
+    n = L.dflash2_verify_sample_workspace_size(4, 8, 1000)
+    assert n >= L.dflash2_verify_workspace_size(4, 8, 1000) and n % 256 == 0
+    assert n >= 4 * 8 * 24
+    p = 0x1000
+
+    def call(**kw):
+        a = dict(batch=4, bs=8, V=1000, drafts=p, lens=None, logits=p, uni=p, T=1.0, top_k=20, top_p=0.95,
+                 acc=p, bonus=p, prob=None, ws=p, nbytes=n)
+        a.update(kw)
+        L.dflash2_verify_sample(None, a["batch"], a["bs"], a["V"], a["drafts"], a["lens"], a["logits"], a["uni"],
+                                a["T"], a["top_k"], a["top_p"], a["acc"], a["bonus"], a["prob"], a["ws"],
+                                a["nbytes"])
+
+    cases = [(dict(bs=1), L.DFLASH2_ERR_SHAPE), (dict(batch=0), L.DFLASH2_ERR_SHAPE),
+             (dict(logits=None), L.DFLASH2_ERR_INVALID_ARG), (dict(bonus=None), L.DFLASH2_ERR_INVALID_ARG),
+             (dict(T=-1.0), L.DFLASH2_ERR_INVALID_ARG), (dict(T=float("nan")), L.DFLASH2_ERR_INVALID_ARG),
+             (dict(T=float("inf")), L.DFLASH2_ERR_INVALID_ARG), (dict(top_k=-1), L.DFLASH2_ERR_INVALID_ARG),
+             (dict(top_p=0.0), L.DFLASH2_ERR_INVALID_ARG), (dict(top_p=float("nan")), L.DFLASH2_ERR_INVALID_ARG),
+             (dict(uni=None), L.DFLASH2_ERR_INVALID_ARG), (dict(nbytes=n - 8), L.DFLASH2_ERR_WORKSPACE),
+             (dict(ws=p + 16), L.DFLASH2_ERR_WORKSPACE)]
+    for kw, status in cases:
+        with pytest.raises(L.DFlash2Error) as e:
+            call(**kw)
+        assert e.value.status == status, kw

@@ -199,3 +199,17 @@ def test_draft_length_rule():
     assert O.draft_lengths(conf, 1.0).tolist() == [0, 0, 0]
     # a confidence equal to p_min does not stop the path
     assert O.draft_lengths(np.array([[0.5, 0.25]]), 0.5).tolist() == [1]
+
+
+def test_distributions_near_the_top_p_bound():
+    z = np.array([math.log(4.0), math.log(2.0), 0.0, 0.0, -math.inf], dtype=np.float32)
+    assert len(O.target_distributions_near(z, 1.0, 0, 0.7, 0.0)) == 1
+    assert len(O.target_distributions_near(z, 1.0, 0, 0.7, 0.01)) == 1      # no group within 0.01
+    near = O.target_distributions_near(z, 1.0, 0, 0.751, 0.01)              # the tied pair sits at 0.75
+    assert len(near) == 2
+    np.testing.assert_allclose(near[0], O.target_distribution(z, 1.0, 0, 0.751), atol=1e-12)
+    kept = sorted(int(np.count_nonzero(q)) for q in near)
+    assert kept == [2, 4]
+    near = O.target_distributions_near(z, 1.0, 0, 0.5, 0.01)                # token 1 sits at 0.5
+    assert sorted(int(np.count_nonzero(q)) for q in near) == [1, 2]
+    assert len(O.target_distributions_near(z, 0.0, 0, 0.5, 0.5)) == 1         # temperature 0: one answer
