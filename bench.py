@@ -74,6 +74,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense27b_bf16")
+    ap.add_argument("--sampling", default=None, metavar="T,TOP_K,TOP_P",
+                    help="verify by rejection sampling at this temperature / top-k / top-p "
+                         "(default: greedy verification)")
+    ap.add_argument("--p-min", type=float, default=None,
+                    help="cut each draft path with the selector confidence rule (draft_p_min)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -86,7 +91,8 @@ def main():
 
     import torch
     import synth
-    from block_speculative_decoding_dflash2_amd import DFlash2, to_device, verify_accept, verify_workspace
+    from block_speculative_decoding_dflash2_amd import (DFlash2, to_device, verify_accept, verify_workspace,
+                                                        verify_sample, verify_sample_workspace)
     from block_speculative_decoding_dflash2_amd.runner import KernelTrace
     from block_speculative_decoding_dflash2_amd.metrics import speculative_metrics
 
@@ -113,7 +119,15 @@ def main():
     drafts = torch.empty((B, bs - 1), dtype=torch.int32, device=dev)
     accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     bonus = torch.empty((B,), dtype=torch.int32, device=dev)
-    vws = verify_workspace(B, bs, V, dev)
+    sampling = None
+    if args.sampling:
+        T_, k_, p_ = args.sampling.split(",")
+        sampling = (float(T_), int(k_), float(p_))
+        vws = verify_sample_workspace(B, bs, V, dev)
+        uniforms = torch.from_numpy(synth.make_uniforms((B, bs), tag=1)).to(dev)
+    else:
+        vws = verify_workspace(B, bs, V, dev)
+    lens = torch.empty((B,), dtype=torch.int32, device=dev) if args.p_min is not None else None
 
     # verifier logits planted around the drafts of a first (untimed) step
     model.draft_block(anchors, taps, offsets, ctx_lens, max_new, kc, vc, workspace=ws,
@@ -125,9 +139,17 @@ def main():
     def step():
         model.draft_block(anchors, taps, offsets, ctx_lens, max_new, kc, vc, workspace=ws,
                           topk_ids=topk_ids, topk_vals=topk_vals)
-        model.select_path(anchors, topk_ids, topk_vals, path_idx=path, draft_tokens=drafts,
-                          want_score=False)
-        verify_accept(drafts, target, workspace=vws, accepted=accepted, bonus=bonus)
+        if lens is None:
+            model.select_path(anchors, topk_ids, topk_vals, path_idx=path, draft_tokens=drafts,
+                              want_score=False)
+        else:
+            model.select_path_stop(anchors, topk_ids, topk_vals, p_min=args.p_min, path_idx=path,
+                                   draft_tokens=drafts, draft_lens=lens)
+        if sampling is None:
+            verify_accept(drafts, target, workspace=vws, accepted=accepted, bonus=bonus)
+        else:
+            verify_sample(drafts, target, uniforms, *sampling, draft_lens=lens, workspace=vws,
+                          accepted=accepted, bonus=bonus)
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -227,7 +249,10 @@ def main():
         "config": {"workload": w.name, "batch": B, "block_size": bs, "hidden": w.hidden,
                    "draft_layers": w.num_layers, "heads": f"{w.num_q_heads}/{w.num_kv_heads}x{w.head_dim}",
                    "ffn": w.ffn, "taps": f"{w.num_taps}x{w.tap_width}", "context": list(w.ctx),
-                   "vocab": V, "top_k": k, "selector_rank": w.rank, "parallelism": "none (1 GPU)"},
+                   "vocab": V, "top_k": k, "selector_rank": w.rank, "parallelism": "none (1 GPU)",
+                   "verification": ("greedy" if sampling is None else
+                                    "rejection sampling T=%g top_k=%d top_p=%g" % sampling),
+                   "draft_p_min": args.p_min},
         "draft_tokens_per_s": round(B * (bs - 1) / s_step, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -637,11 +637,13 @@ dflash2_status greedy_impl(hipStream_t stream, int32_t batch, int32_t block_size
   return check_launch(name);
 }
 
-// Row results of the sampled verification: theta, max key [rows] u32; kept
-// mass S, draft weight Ed [rows] u64.
+// Row results of the sampled verification: theta, max key, kept count
+// [rows] u32; kept mass S, draft weight Ed [rows] u64; kept ids [rows][SV_OUT]
+// u32 and weights [rows][SV_OUT] u64.
 size_t sample_ws_bytes(int B, int bs) {
   const size_t rows = size_t(B) * bs;
-  return align_up(rows * 4) * 2 + align_up(rows * 8) * 2;
+  return align_up(rows * 4) * 3 + align_up(rows * 8) * 2 + align_up(rows * SV_OUT * 4) +
+         align_up(rows * SV_OUT * 8);
 }
 }  // namespace
 
@@ -711,10 +713,15 @@ dflash2_status dflash2_verify_sample(hipStream_t stream, int32_t batch, int32_t 
     a.top_p = top_p >= 1.0f ? 1.0f : top_p;
     a.qscale = std::ldexp(1.0f, 52 - bits);
     a.B = batch; a.bs = block_size; a.V = vocab;
-    a.theta = reinterpret_cast<uint32_t*>(ws);
-    a.mkey = reinterpret_cast<uint32_t*>(ws + align_up(rows * 4));
-    a.S = reinterpret_cast<uint64_t*>(ws + 2 * align_up(rows * 4));
-    a.Ed = reinterpret_cast<uint64_t*>(ws + 2 * align_up(rows * 4) + align_up(rows * 8));
+    size_t off = 0;
+    auto carve = [&](size_t bytes) { char* q = ws + off; off += align_up(bytes); return q; };
+    a.theta = reinterpret_cast<uint32_t*>(carve(rows * 4));
+    a.mkey = reinterpret_cast<uint32_t*>(carve(rows * 4));
+    a.kept_n = reinterpret_cast<int32_t*>(carve(rows * 4));
+    a.S = reinterpret_cast<uint64_t*>(carve(rows * 8));
+    a.Ed = reinterpret_cast<uint64_t*>(carve(rows * 8));
+    a.kept_id = reinterpret_cast<uint32_t*>(carve(rows * SV_OUT * 4));
+    a.kept_w = reinterpret_cast<uint64_t*>(carve(rows * SV_OUT * 8));
     a.accepted = accepted; a.bonus = bonus; a.draft_prob = draft_prob;
     traced(stream, DFLASH2_K_SAMPLE_ROWS, int64_t(rows) * vocab * 4 + int64_t(rows) * 24, 0,
            [&] { launch_sample_rows(a, stream); });

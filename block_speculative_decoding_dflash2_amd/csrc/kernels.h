@@ -157,8 +157,11 @@ struct SampleArgs {
   float temp; int top_k; float top_p; float qscale;   // top_k 0 = off, top_p >= 1 = off
   int B, bs, V;
   uint32_t* theta; uint32_t* mkey; uint64_t* S; uint64_t* Ed;   // [B*bs] row results
+  int32_t* kept_n; uint32_t* kept_id; uint64_t* kept_w;           // [B*bs], [B*bs][SV_OUT] x2
   int32_t* accepted; int32_t* bonus; float* draft_prob;
 };
+// Kept sets of at most this many entries are handed from the row pass to the draw.
+constexpr int SV_OUT = 256;
 
 // Activation rows above which the LDS-tiled, compute-bound GEMMs are used.
 constexpr int kTiledMinRows = 64;

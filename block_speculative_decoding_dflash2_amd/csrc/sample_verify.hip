@@ -189,9 +189,9 @@ __device__ void sv_hist(SvShared& sh, const float* z, int V, bool vec, int level
   __syncthreads();
 }
 
-// Collects every element with key >= lo into the list (the caller knows the
-// count fits) and sorts the list descending (value desc, id asc).
-__device__ void sv_collect_sort(SvShared& sh, const float* z, int V, bool vec, uint32_t lo) {
+// Collects every element with key >= lo into the list (entries past the
+// capacity are counted, not stored); returns the count.
+__device__ uint32_t sv_collect(SvShared& sh, const float* z, int V, bool vec, uint32_t lo) {
   if (threadIdx.x == 0) sh.nlist = 0u;
   __syncthreads();
   sv_for_row(z, V, vec, [&](int id, float x) {
@@ -202,7 +202,13 @@ __device__ void sv_collect_sort(SvShared& sh, const float* z, int V, bool vec, u
     }
   });
   __syncthreads();
-  const int n = int(min(sh.nlist, uint32_t(SV_CAP)));
+  const uint32_t n = sh.nlist;
+  __syncthreads();
+  return n;
+}
+
+// Sorts the first n (<= capacity) list entries descending (value desc, id asc).
+__device__ void sv_sort(SvShared& sh, int n) {
   int N = 2;
   while (N < n) N <<= 1;
   for (int i = n + threadIdx.x; i < N; i += SV_THREADS) sh.list[i] = 0ull;
@@ -229,8 +235,8 @@ __device__ void sv_collect_sort(SvShared& sh, const float* z, int V, bool vec, u
 // X).  Returns (through sh) nkeep = the kept prefix length and the kept
 // mass.  n = entries of the kept set held in the list; S_known = 0 means
 // the list holds the whole kept set and its total is the kept mass.
-__device__ void sv_list_top_p(SvShared& sh, int n, const SvWeight& W, bool top_p_on, float top_p,
-                              uint64_t S_known, uint32_t& theta, uint64_t& S_final) {
+__device__ int sv_list_top_p(SvShared& sh, int n, const SvWeight& W, bool top_p_on, float top_p,
+                             uint64_t S_known, uint32_t& theta, uint64_t& S_final) {
   const int t = threadIdx.x;
   uint64_t w0 = 0, w1 = 0;
   if (2 * t < n) w0 = W(uint32_t(sh.list[2 * t] >> 32));
@@ -262,6 +268,7 @@ __device__ void sv_list_top_p(SvShared& sh, int n, const SvWeight& W, bool top_p
   const uint64_t wl = W(theta);
   S_final = sh.pre[nkeep - 1] + wl;
   __syncthreads();
+  return nkeep;
 }
 
 }  // namespace
@@ -280,14 +287,44 @@ __global__ __launch_bounds__(SV_THREADS) void sample_rows_kernel(SampleArgs p) {
   const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0;
   const int t = threadIdx.x;
 
-  // ---- pass A: row maximum and the level-0 count histogram
-  sv_clear(sh, false);
-  uint32_t mk = 0u;
-  sv_for_row(z, V, vec, [&](int, float x) {
-    const uint32_t k = sv_key(sv_clean(x));
-    mk = k > mk ? k : mk;
-    atomicAdd(&sh.cnt[k >> 21], 1u);
-  });
+  const bool topk_on = p.top_k > 0;
+  const bool top_p_on = p.top_p < 1.0f;
+  bool in_list = false;      // the list holds the kept set from the top, sorted
+  int nkept = V;             // size of the kept set (top-k)
+  uint32_t tk = 0u;          // kept set = keys >= tk
+  uint32_t mk = 0u;          // the row's largest key
+  if (topk_on) {
+    // ---- top-k in one pass over the row.  The first ns ids estimate where
+    // the k largest end (the level-0 bin holding the sample's j-th largest,
+    // j = k scaled to the sample plus a margin); the pass then takes the row
+    // maximum and collects every element at or above that bin.  Exact
+    // whenever at least k elements were collected (the k-th largest and all
+    // its ties are then in the list) and they fit it; otherwise the exact
+    // radix select below runs.
+    const int ns = vec ? (min(V, max(4096, V / 16)) & ~3) : min(V, max(4096, V / 16));
+    sv_clear(sh, false);
+    sv_for_row(z, ns, vec, [&](int, float x) { atomicAdd(&sh.cnt[sv_key(sv_clean(x)) >> 21], 1u); });
+    __syncthreads();
+    const int target = min(ns, int((int64_t(p.top_k) * ns + V - 1) / V) + 8);
+    sv_find(sh, SV_BINS, false, double(target), 0ull);
+    const uint32_t lo = sh.fbin << 21;
+    if (t == 0) sh.nlist = 0u;
+    __syncthreads();
+    sv_for_row(z, V, vec, [&](int id, float x) {
+      const uint32_t k = sv_key(sv_clean(x));
+      mk = k > mk ? k : mk;
+      if (k >= lo) {
+        const uint32_t slot = atomicAdd(&sh.nlist, 1u);
+        if (slot < uint32_t(SV_CAP)) sh.list[slot] = (uint64_t(k) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(id));
+      }
+    });
+  } else {
+    // ---- row maximum
+    sv_for_row(z, V, vec, [&](int, float x) {
+      const uint32_t k = sv_key(sv_clean(x));
+      mk = k > mk ? k : mk;
+    });
+  }
   {
     uint32_t v = mk;
 #pragma unroll
@@ -303,16 +340,25 @@ __global__ __launch_bounds__(SV_THREADS) void sample_rows_kernel(SampleArgs p) {
   }
   SvWeight W;
   W.mkey = mk; W.m = sv_val(mk); W.temp = p.temp; W.qscale = p.qscale;
-
-  // ---- top-k: the k-th largest key (with multiplicity)
-  const bool topk_on = p.top_k > 0;
-  const bool top_p_on = p.top_p < 1.0f;
-  bool in_list = false;      // the list holds the kept set from the top, sorted
-  int nkept = V;             // size of the kept set (top-k)
-  uint32_t tk = 0u;          // kept set = keys >= tk
   if (topk_on) {
+    const uint32_t n = sh.nlist;
+    if (n >= uint32_t(p.top_k) && n <= uint32_t(SV_CAP)) {
+      sv_sort(sh, int(n));
+      tk = uint32_t(sh.list[p.top_k - 1] >> 32);
+      if (t == 0) sh.red[0] = uint32_t(p.top_k);
+      __syncthreads();
+      for (int j = p.top_k + t; j < int(n); j += SV_THREADS)
+        if (uint32_t(sh.list[j] >> 32) >= tk) atomicMax(&sh.red[0], uint32_t(j + 1));
+      __syncthreads();
+      nkept = int(sh.red[0]);
+      __syncthreads();
+      in_list = true;
+    }
+  }
+  if (topk_on && !in_list) {
     uint32_t prefix = 0u;
     uint64_t base = 0ull;
+    sv_hist(sh, z, V, vec, 0, 0u, 0u, nullptr);
     for (int level = 0; level < 3; ++level) {
       if (level > 0) sv_hist(sh, z, V, vec, level, prefix, 0u, nullptr);
       sv_find(sh, level == 2 ? 1024 : SV_BINS, false, double(p.top_k), base);
@@ -322,7 +368,8 @@ __global__ __launch_bounds__(SV_THREADS) void sample_rows_kernel(SampleArgs p) {
       prefix = level == 0 ? bin : ((prefix << (level == 1 ? 11 : 10)) | bin);
       base += above;
       if (base + hbin <= uint64_t(SV_CAP)) {
-        sv_collect_sort(sh, z, V, vec, prefix << sv_shift(level));
+        sv_collect(sh, z, V, vec, prefix << sv_shift(level));
+        sv_sort(sh, int(base + hbin));
         tk = uint32_t(sh.list[min(p.top_k, int(base + hbin)) - 1] >> 32);
         // kept = list entries with key >= tk (the k-th and its ties)
         if (t == 0) sh.red[0] = uint32_t(p.top_k);
@@ -340,16 +387,18 @@ __global__ __launch_bounds__(SV_THREADS) void sample_rows_kernel(SampleArgs p) {
         nkept = int(base + hbin);
       }
     }
-  } else if (V <= SV_CAP) {
-    sv_collect_sort(sh, z, V, vec, 0u);
+  } else if (!topk_on && V <= SV_CAP) {
+    sv_collect(sh, z, V, vec, 0u);
+    sv_sort(sh, V);
     in_list = true;
   }
 
   // ---- masses and top-p
   uint32_t theta;
   uint64_t S_final;
+  int nlisted = 0;           // kept set held, sorted, in list[0, nlisted) (0: not held)
   if (in_list) {
-    sv_list_top_p(sh, nkept, W, top_p_on, p.top_p, 0ull, theta, S_final);
+    nlisted = sv_list_top_p(sh, nkept, W, top_p_on, p.top_p, 0ull, theta, S_final);
   } else {
     sv_hist(sh, z, V, vec, 0, 0u, tk, &W);
     if (!top_p_on) {
@@ -378,8 +427,9 @@ __global__ __launch_bounds__(SV_THREADS) void sample_rows_kernel(SampleArgs p) {
         base_c += ac;
         if (base_c + bc <= uint64_t(SV_CAP)) {
           const uint32_t lo = prefix << sv_shift(level);
-          sv_collect_sort(sh, z, V, vec, lo > tk ? lo : tk);
-          sv_list_top_p(sh, int(base_c + bc), W, true, p.top_p, S_K, theta, S_final);
+          sv_collect(sh, z, V, vec, lo > tk ? lo : tk);
+          sv_sort(sh, int(base_c + bc));
+          nlisted = sv_list_top_p(sh, int(base_c + bc), W, true, p.top_p, S_K, theta, S_final);
           break;
         }
         if (level == 2) {
@@ -390,7 +440,17 @@ __global__ __launch_bounds__(SV_THREADS) void sample_rows_kernel(SampleArgs p) {
     }
   }
 
+  // hand a small kept set to the draw (ids and weights, value desc)
+  const bool hand = nlisted > 0 && nlisted <= SV_OUT;
+  if (hand) {
+    for (int j = t; j < nlisted; j += SV_THREADS) {
+      const uint64_t e = sh.list[j];
+      p.kept_id[int64_t(row) * SV_OUT + j] = 0xFFFFFFFFu - uint32_t(e);
+      p.kept_w[int64_t(row) * SV_OUT + j] = W(uint32_t(e >> 32));
+    }
+  }
   if (t == 0) {
+    p.kept_n[row] = hand ? nlisted : 0;
     uint64_t Ed = 0ull;
     if (i < len) {
       const int d = p.drafts[int64_t(b) * P + i];
@@ -406,10 +466,15 @@ __global__ __launch_bounds__(SV_THREADS) void sample_rows_kernel(SampleArgs p) {
   }
 }
 
-// One block of 1024 per sequence: the accepted prefix, then the bonus draw
-// by an exact fixed-point prefix scan over the stop row in id order.
+// One block of 1024 per sequence: the accepted prefix, then the bonus draw.
+// A kept set the row pass handed over (at most SV_OUT entries) is drawn from
+// directly: entry j is the draw when the mass of the entries with ids <= its
+// own first exceeds R.  Otherwise an exact fixed-point prefix scan walks the
+// stop row in id order, 16 ids per thread per step.
 __global__ __launch_bounds__(SV_THREADS) void sample_pick_kernel(SampleArgs p) {
   __shared__ uint64_t scan[2 * SV_WAVES];
+  __shared__ uint32_t kid[SV_OUT];
+  __shared__ uint64_t kw[SV_OUT];
   __shared__ int s_n, s_found;
   __shared__ uint64_t s_best;
   const int b = blockIdx.x, t = threadIdx.x;
@@ -437,59 +502,87 @@ __global__ __launch_bounds__(SV_THREADS) void sample_pick_kernel(SampleArgs p) {
   const int64_t row = r0 + n;
   const bool residual = n < len;
   const int d = residual ? p.drafts[int64_t(b) * P + n] : -1;
-  const uint32_t theta = p.theta[row];
-  SvWeight W;
-  W.mkey = p.mkey[row]; W.m = sv_val(W.mkey); W.temp = p.temp; W.qscale = p.qscale;
   const uint64_t S = p.S[row] - (residual ? p.Ed[row] : 0ull);
   double v = double(p.uni[r0 + P]);
   if (!(v >= 0.0)) v = 0.0;
   const double Rd = floor(v * double(S));
   const uint64_t R = Rd >= double(S) ? S : uint64_t(Rd);
-  const int V = p.V;
-  const float* z = p.logits + row * V;
-  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0;
-  uint64_t running = 0ull, best = 0ull;
-  for (int j0 = 0; j0 < V; j0 += 4 * SV_THREADS) {
-    const int j = j0 + 4 * t;
-    float x[4];
-    if (vec && j + 3 < V) {
-      const f32x4 q = *reinterpret_cast<const f32x4*>(z + j);
-      x[0] = q[0]; x[1] = q[1]; x[2] = q[2]; x[3] = q[3];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = j + e < V ? z[j + e] : -INFINITY;
+  const int nk = p.kept_n[row];
+  if (nk > 0) {
+    if (t < nk) {
+      const uint32_t id = p.kept_id[row * SV_OUT + t];
+      kid[t] = id;
+      kw[t] = id == uint32_t(d) ? 0ull : p.kept_w[row * SV_OUT + t];
     }
-    uint64_t w[4], s = 0ull;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t k = sv_key(sv_clean(x[e]));
-      const bool elig = j + e < V && j + e != d && k >= theta;
-      w[e] = elig ? W(k) : 0ull;
-      s += w[e];
-      if (elig) {
-        const uint64_t rk = (uint64_t(k) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(j + e));
-        best = rk > best ? rk : best;
-      }
-    }
-    uint64_t ex = s, dummy = 0ull, tot, tot2;
-    sv_scan2(ex, dummy, tot, tot2, scan);
-    const uint64_t c0 = running + ex;
-    if (c0 <= R && R < c0 + s) {
-      uint64_t c = c0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c += w[e];
-        if (c > R) { s_found = j + e; break; }
-      }
-    }
-    running += tot;
     __syncthreads();
-    if (s_found >= 0) break;
-  }
-  if (s_found < 0) {
-    // no draw (only for a uniform outside [0, 1)): the most likely eligible id
-    atomicMax(reinterpret_cast<unsigned long long*>(&s_best), (unsigned long long)best);
+    if (t < nk && kw[t] > 0ull) {
+      const uint32_t me = kid[t];
+      uint64_t cum = 0ull;
+      for (int i = 0; i < nk; ++i) cum += kid[i] <= me ? kw[i] : 0ull;
+      if (cum > R && cum - kw[t] <= R) s_found = int(me);
+    }
     __syncthreads();
+    if (t == 0 && s_found < 0) {
+      // no draw (only for a uniform outside [0, 1)): the most likely
+      // eligible id = the first in (value desc, id asc) order
+      for (int i = 0; i < nk; ++i)
+        if (kid[i] != uint32_t(d)) { s_best = (uint64_t(1) << 32) | uint64_t(0xFFFFFFFFu - kid[i]); break; }
+    }
+    __syncthreads();
+  } else {
+    const uint32_t theta = p.theta[row];
+    SvWeight W;
+    W.mkey = p.mkey[row]; W.m = sv_val(W.mkey); W.temp = p.temp; W.qscale = p.qscale;
+    const int V = p.V;
+    const float* z = p.logits + row * V;
+    const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0;
+    uint64_t running = 0ull, best = 0ull;
+    for (int j0 = 0; j0 < V; j0 += 16 * SV_THREADS) {
+      const int j = j0 + 16 * t;     // this thread's 16 consecutive ids
+      float x[16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int jj = j + 4 * u;
+        if (vec && jj + 3 < V) {
+          const f32x4 q = *reinterpret_cast<const f32x4*>(z + jj);
+          x[4 * u] = q[0]; x[4 * u + 1] = q[1]; x[4 * u + 2] = q[2]; x[4 * u + 3] = q[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * u + e] = jj + e < V ? z[jj + e] : -INFINITY;
+        }
+      }
+      uint64_t s = 0ull;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t k = sv_key(sv_clean(x[e]));
+        const bool elig = j + e < V && j + e != d && k >= theta;
+        s += elig ? W(k) : 0ull;
+        if (elig) {
+          const uint64_t rk = (uint64_t(k) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(j + e));
+          best = rk > best ? rk : best;
+        }
+      }
+      uint64_t ex = s, dummy = 0ull, tot, tot2;
+      sv_scan2(ex, dummy, tot, tot2, scan);
+      const uint64_t c0 = running + ex;
+      if (c0 <= R && R < c0 + s) {
+        uint64_t c = c0;
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t k = sv_key(sv_clean(x[e]));
+          const bool elig = j + e < V && j + e != d && k >= theta;
+          c += elig ? W(k) : 0ull;
+          if (c > R) { s_found = j + e; break; }
+        }
+      }
+      running += tot;
+      __syncthreads();
+      if (s_found >= 0) break;
+    }
+    if (s_found < 0) {
+      // no draw (only for a uniform outside [0, 1)): the most likely eligible id
+      atomicMax(reinterpret_cast<unsigned long long*>(&s_best), (unsigned long long)best);
+      __syncthreads();
+    }
   }
   if (t == 0) {
     int g = s_found;

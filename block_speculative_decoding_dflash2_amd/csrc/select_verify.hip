@@ -254,10 +254,30 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
     if (lane < k) {
       const int cj = ids[t * k + lane];
       const bool okp = prev >= 0 && prev < V, okc = cj >= 0 && cj < V;
+      const float* ta = p.tl + int64_t(okp ? prev : 0) * r;
+      const float* tb = p.tr + int64_t(okc ? cj : 0) * r;
       float acc = 0.0f;
-      for (int m = 0; m < r; ++m) {
-        const float a = okp ? p.tl[int64_t(prev) * r + m] : 0.0f;
-        const float c = okc ? p.tr[int64_t(cj) * r + m] : 0.0f;
+      int m = 0;
+      if (vec4) {
+        for (; m + 16 <= r; m += 16) {
+          f32x4 a4[4], c4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            a4[u] = okp ? *reinterpret_cast<const f32x4*>(ta + m + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+            c4[u] = okc ? *reinterpret_cast<const f32x4*>(tb + m + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float prod = a4[u][e] * c4[u][e];
+              acc = acc + prod;
+            }
+        }
+      }
+      for (; m < r; ++m) {
+        const float a = okp ? ta[m] : 0.0f;
+        const float c = okc ? tb[m] : 0.0f;
         const float prod = a * c;
         acc = acc + prod;
       }
