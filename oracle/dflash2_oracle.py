@@ -729,7 +729,8 @@ def step(w, W, inp, target_logits_fn=None) -> Dict[str, np.ndarray]:
 # ----------------------------------------------------------------------------
 
 
-def decode_loop(w, W, inp, steps: int, target_logits_fn, verified_taps_fn) -> Dict[str, list]:
+def decode_loop(w, W, inp, steps: int, target_logits_fn, verified_taps_fn, sampling=None,
+                uniforms_fn=None, p_min=None, n_min: int = 0, n_max=None) -> Dict[str, list]:
     """`steps` draft -> select -> verify rounds with the state carried over.
 
     [LC §Prerequisites and §Complete Runnable Code: the target scores the
@@ -745,15 +746,18 @@ def decode_loop(w, W, inp, steps: int, target_logits_fn, verified_taps_fn) -> Di
 
     target_logits_fn(step, drafts) -> [B, bs, V] float32 verifier logits;
     verified_taps_fn(starts, counts) -> (taps Tensor, offsets) for positions
-    starts[b] .. starts[b] + counts[b] - 1.  Returns per-step lists of
-    drafts, accepted, bonus and ctx_lens (before the step)."""
+    starts[b] .. starts[b] + counts[b] - 1.  sampling = (temperature, top_k,
+    top_p) verifies by rejection sampling (O9) with uniforms_fn(step) ->
+    [B, bs]; p_min cuts each path with the confidence rule (O8).  Returns
+    per-step lists of drafts, lens, accepted, bonus, ctx_lens (before the
+    step) and margin (sampled decisions' distance from their thresholds)."""
     B = len(inp.anchors)
     k_cache, v_cache = new_cache(w, B, inp.k_ctx, inp.v_ctx)
     anchors = np.asarray(inp.anchors).copy()
     ctx = np.asarray(inp.ctx_lens).astype(np.int64).copy()
     taps, offsets = inp.taps, np.asarray(inp.new_offsets)
     P = w.block_size - 1
-    rec = {"drafts": [], "accepted": [], "bonus": [], "ctx_lens": []}
+    rec = {"drafts": [], "lens": [], "accepted": [], "bonus": [], "ctx_lens": [], "margin": []}
     for s in range(steps):
         append_context(w, W, k_cache, v_cache, taps, offsets, ctx)
         fwd = draft_block(w, W, k_cache, v_cache, anchors, ctx)
@@ -761,10 +765,21 @@ def decode_loop(w, W, inp, steps: int, target_logits_fn, verified_taps_fn) -> Di
         ids, _ = topk(zeta.astype(np.float32).reshape(-1, w.vocab), w.top_k)
         z = logit_transform(zeta, w.output_multiplier, w.final_logit_softcapping).astype(np.float32)
         vals = np.take_along_axis(z.reshape(-1, w.vocab), ids.astype(np.int64), axis=1)
-        sel = select_path(anchors, ids.reshape(B, P, w.top_k), vals.reshape(B, P, w.top_k),
-                          W.sel_tl.data, W.sel_tr.data)
-        ver = verify_accept(sel["drafts"], target_logits_fn(s, sel["drafts"]))
+        ids3, vals3 = ids.reshape(B, P, w.top_k), vals.reshape(B, P, w.top_k)
+        sel = select_path(anchors, ids3, vals3, W.sel_tl.data, W.sel_tr.data)
+        lens = np.full(B, P, dtype=np.int32)
+        if p_min is not None:
+            conf = path_confidence(anchors, ids3, vals3, sel["path"], W.sel_tl.data, W.sel_tr.data)
+            lens = draft_lengths(conf, p_min, n_min, n_max)
+        tz = target_logits_fn(s, sel["drafts"])
+        if sampling is None:
+            ver = verify_accept_len(sel["drafts"], tz, lens)
+            ver["margin"] = np.full(B, np.inf)
+        else:
+            ver = verify_sample(sel["drafts"], tz, uniforms_fn(s), *sampling, draft_lens=lens)
         rec["drafts"].append(sel["drafts"])
+        rec["lens"].append(lens)
+        rec["margin"].append(ver["margin"])
         rec["accepted"].append(ver["accepted"])
         rec["bonus"].append(ver["bonus"])
         rec["ctx_lens"].append(ctx.copy())

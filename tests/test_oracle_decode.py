@@ -60,3 +60,37 @@ def test_acceptance_by_position_matches_histogram():
     hist = m["acceptance_histogram"]
     for i, r in enumerate(m["acceptance_by_position"]):
         assert r == sum(hist[i + 1:]) / 5
+
+
+def test_sampled_loop_at_vanishing_temperature_is_the_greedy_loop():
+    """Planted argmaxes stand a full logit above the rest, so at temperature
+    1e-3 each row is a point mass on its argmax and the sampled loop must
+    follow the greedy loop round for round."""
+    w = TINY_FP32.replace(batch=2, agree=("const", 0.6), spare_context=STEPS * 8)
+    W, inp, greedy = _loop(w)
+    sampled = O.decode_loop(w, W, inp, STEPS,
+                            lambda s, d: synth.make_target_logits(w, d, tag=1000 + s),
+                            lambda starts, counts: synth.make_verified_taps(w, starts, counts),
+                            sampling=(1e-3, 0, 1.0),
+                            uniforms_fn=lambda s: synth.make_uniforms((w.batch, w.block_size), tag=s))
+    for s in range(STEPS):
+        for k in ("drafts", "accepted", "bonus", "ctx_lens"):
+            assert np.array_equal(sampled[k][s], greedy[k][s]), (k, s)
+
+
+def test_p_min_one_cuts_every_path_to_n_min():
+    """p_min = 1 stops at the first position allowed (a confidence is below 1
+    unless one candidate takes all the mass), so every round proposes n_min
+    drafts and the context grows by at most n_min + 1."""
+    w = TINY_FP32.replace(batch=2, agree=("const", 1.0), spare_context=STEPS * 8)
+    W = synth.make_weights(w)
+    inp = synth.make_step_inputs(w)
+    rec = O.decode_loop(w, W, inp, STEPS,
+                        lambda s, d: synth.make_target_logits(w, d, tag=1000 + s),
+                        lambda starts, counts: synth.make_verified_taps(w, starts, counts),
+                        p_min=1.0, n_min=2)
+    for s in range(STEPS):
+        assert np.all(rec["lens"][s] == 2)
+        assert np.all(rec["accepted"][s] == 2)          # the target agrees with every draft
+        if s + 1 < STEPS:
+            assert np.array_equal(rec["ctx_lens"][s + 1], rec["ctx_lens"][s] + 3)
