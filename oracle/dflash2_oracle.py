@@ -693,6 +693,92 @@ def top_p_margin(z_row, temperature, top_k, top_p) -> float:
 
 
 # ----------------------------------------------------------------------------
+# O10: training-side forward losses.
+# ----------------------------------------------------------------------------
+
+
+def position_weights(block_size: int, gamma: float) -> np.ndarray:
+    """w_k = exp(-(k - 1) / gamma) for supervised slots k = 1 .. bs-1
+    ([AM §Objective]); gamma = inf gives equal weights."""
+    k = np.arange(1, block_size, dtype=np.float64)
+    return np.exp(-(k - 1.0) / gamma)
+
+
+def block_losses(anchors, labels, logits, cand_ids, cand_vals, tl, tr, gamma: float,
+                 selector_loss_weight: float, multiplier: float = 1.0, softcap: float = 0.0) -> Dict:
+    """The DFlash 2 training objective evaluated forward on given logits.
+
+    [AM §Objective: slots 1..bs-1 are supervised, their cross-entropy
+    weighted by exp(-(k-1)/loss_decay_gamma); DFlash 2 adds, weighted by
+    selector_loss_weight, a cross-entropy over each position's top-k
+    candidates scored against the ground-truth predecessor; positions whose
+    true token missed the candidates carry no selector signal and are
+    reported as candidate_recall.  AM §Key Config Fields: the logit
+    transform applies in training too.]  Readings:
+      L1  logits [B, bs-1, V] are the pre-transform float32 logits; CE uses
+          the transformed ones (logit_transform), in float64;
+      L2  labels [B, bs-1] are the true tokens of slots 1..bs-1; a label
+          outside [0, V) marks a position as unsupervised (no terms, not
+          counted anywhere);
+      L3  block loss = sum_k w_k CE_k / sum_k w_k over supervised positions;
+      L4  selector score of candidate j at slot k: the lattice's float32
+          pi(true_{k-1}, c_kj) + z_kj, with true_0 = the anchor and true_{k-1}
+          = label_{k-1}; CE_sel = logsumexp_j s - s_true (float64 on the
+          float32 scores); a position has a selector signal when its label is
+          among its candidates and its predecessor is known (anchor, or a
+          supervised label);
+      L5  selector loss = mean CE_sel over positions with a signal (0 when
+          none); candidate_recall = supervised positions whose label is among
+          the candidates / supervised positions; total = block loss +
+          selector_loss_weight * selector loss.
+    Returns block_ce [B, P], selector_ce [B, P] (NaN without a signal),
+    in_cands [B, P] bool and the scalars total, block, selector, recall."""
+    labels = np.asarray(labels)
+    z = np.asarray(logits, dtype=np.float32)
+    cand_ids = np.asarray(cand_ids)
+    cand_vals = np.asarray(cand_vals, dtype=np.float32)
+    B, P, V = z.shape
+    zt = logit_transform(z.astype(np.float64), multiplier, softcap)
+    w = position_weights(P + 1, gamma)
+    block_ce = np.full((B, P), np.nan)
+    sel_ce = np.full((B, P), np.nan)
+    in_c = np.zeros((B, P), dtype=bool)
+    num = den = 0.0
+    sel_sum, sel_n, sup_n, hit_n = 0.0, 0, 0, 0
+    for b in range(B):
+        for k in range(P):
+            lab = int(labels[b, k])
+            if not 0 <= lab < V:
+                continue
+            row = zt[b, k]
+            m = row.max()
+            lse = m + np.log(np.exp(row - m).sum())
+            block_ce[b, k] = lse - row[lab]
+            num += w[k] * block_ce[b, k]
+            den += w[k]
+            sup_n += 1
+            hit = np.nonzero(cand_ids[b, k] == lab)[0]
+            if hit.size == 0:
+                continue
+            in_c[b, k] = True
+            hit_n += 1
+            prev = int(anchors[b]) if k == 0 else int(labels[b, k - 1])
+            if not 0 <= prev < V:
+                continue
+            s = (pair_scores(tl, tr, [prev], cand_ids[b, k])[0] + cand_vals[b, k]).astype(np.float32)
+            s = s.astype(np.float64)
+            ms = s.max()
+            sel_ce[b, k] = ms + np.log(np.exp(s - ms).sum()) - s[int(hit[0])]
+            sel_sum += sel_ce[b, k]
+            sel_n += 1
+    block = num / den if den > 0 else 0.0
+    selector = sel_sum / sel_n if sel_n else 0.0
+    recall = hit_n / sup_n if sup_n else 0.0
+    return {"block_ce": block_ce, "selector_ce": sel_ce, "in_cands": in_c, "block": block,
+            "selector": selector, "recall": recall, "total": block + selector_loss_weight * selector}
+
+
+# ----------------------------------------------------------------------------
 # The whole step.
 # ----------------------------------------------------------------------------
 
