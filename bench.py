@@ -79,6 +79,9 @@ def main():
                          "(default: greedy verification)")
     ap.add_argument("--p-min", type=float, default=None,
                     help="cut each draft path with the selector confidence rule (draft_p_min)")
+    ap.add_argument("--losses", default=None, metavar="GAMMA,WEIGHT",
+                    help="also evaluate the forward training losses on the step's logits (the draft "
+                         "then writes its float32 logits) with synthetic labels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -128,6 +131,13 @@ def main():
     else:
         vws = verify_workspace(B, bs, V, dev)
     lens = torch.empty((B,), dtype=torch.int32, device=dev) if args.p_min is not None else None
+    dlogits = labels = None
+    if args.losses:
+        gamma, wsel = (float(x) for x in args.losses.split(","))
+        dlogits = torch.empty((B, bs - 1, V), dtype=torch.float32, device=dev)
+        rng = np.random.default_rng(5)
+        labels = torch.from_numpy(rng.integers(0, V, (B, bs - 1)).astype(np.int32)).to(dev)
+        loss_out = torch.empty((4,), dtype=torch.float32, device=dev)
 
     # verifier logits planted around the drafts of a first (untimed) step
     model.draft_block(anchors, taps, offsets, ctx_lens, max_new, kc, vc, workspace=ws,
@@ -138,7 +148,9 @@ def main():
 
     def step():
         model.draft_block(anchors, taps, offsets, ctx_lens, max_new, kc, vc, workspace=ws,
-                          topk_ids=topk_ids, topk_vals=topk_vals)
+                          topk_ids=topk_ids, topk_vals=topk_vals, debug_logits=dlogits)
+        if dlogits is not None:
+            model.draft_losses(anchors, labels, dlogits, topk_ids, topk_vals, gamma, wsel, losses=loss_out)
         if lens is None:
             model.select_path(anchors, topk_ids, topk_vals, path_idx=path, draft_tokens=drafts,
                               want_score=False)
@@ -252,7 +264,7 @@ def main():
                    "vocab": V, "top_k": k, "selector_rank": w.rank, "parallelism": "none (1 GPU)",
                    "verification": ("greedy" if sampling is None else
                                     "rejection sampling T=%g top_k=%d top_p=%g" % sampling),
-                   "draft_p_min": args.p_min},
+                   "draft_p_min": args.p_min, "forward_losses": args.losses},
         "draft_tokens_per_s": round(B * (bs - 1) / s_step, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

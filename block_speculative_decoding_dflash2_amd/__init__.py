@@ -8,7 +8,7 @@ no CPU fallback."""
 import importlib
 
 _FROM_LIB = ("DFlash2Error", "EXPORTED", "LIB_PATH", "dflash2_create", "dflash2_destroy",
-             "dflash2_draft_block", "dflash2_last_error", "dflash2_select_path", "dflash2_select_path_stop",
+             "dflash2_draft_block", "dflash2_draft_losses", "dflash2_draft_losses_workspace_size", "dflash2_last_error", "dflash2_select_path", "dflash2_select_path_stop",
              "dflash2_verify_accept", "dflash2_verify_sample", "dflash2_verify_sample_workspace_size",
              "dflash2_verify_workspace_size", "dflash2_workspace_size")
 _FROM_RUNNER = ("DFlash2", "config_struct", "to_device", "verify_accept", "verify_sample", "verify_sample_workspace",

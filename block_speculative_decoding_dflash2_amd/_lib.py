@@ -42,7 +42,7 @@ class dflash2_weights(ctypes.Structure):
 
 KERNEL_KINDS = ("gemm", "lmhead_topk", "topk_merge", "norm", "qkv_epilogue", "kv_append", "swiglu",
                 "attention", "attn_combine", "select", "verify_partial", "verify_final", "sample_rows",
-                "sample_pick")
+                "sample_pick", "loss_rows", "loss_seq")
 
 
 class dflash2_trace_entry(ctypes.Structure):
@@ -78,6 +78,9 @@ def _load():
                                    c_float, i32p, i32p, f32p, vp, c_size_t], c_int32),
         "dflash2_verify_accept": ([vp, c_int32, c_int32, c_int32, i32p, f32p, i32p, i32p, i32p, vp,
                                    c_size_t], c_int32),
+        "dflash2_draft_losses_workspace_size": ([c_int32, c_int32, c_int32, POINTER(c_size_t)], c_int32),
+        "dflash2_draft_losses": ([vp, vp, c_int32, i32p, i32p, f32p, i32p, f32p, c_float, c_float, f32p, f32p,
+                                  f32p, vp, c_size_t], c_int32),
         "dflash2_trace_attach": ([POINTER(dflash2_trace_entry), c_int32], c_int32),
         "dflash2_trace_detach": ([], c_int32),
         "dflash2_last_error": ([], ctypes.c_char_p),
@@ -93,6 +96,7 @@ lib = _load()
 EXPORTED = ("dflash2_create", "dflash2_destroy", "dflash2_workspace_size", "dflash2_draft_block",
             "dflash2_select_path", "dflash2_select_path_stop", "dflash2_verify_workspace_size",
             "dflash2_verify_accept", "dflash2_verify_sample_workspace_size", "dflash2_verify_sample",
+            "dflash2_draft_losses_workspace_size", "dflash2_draft_losses",
             "dflash2_trace_attach", "dflash2_trace_detach", "dflash2_last_error")
 
 
@@ -174,3 +178,16 @@ def dflash2_verify_sample(stream, batch, block_size, vocab, draft_tokens, draft_
     _check(lib.dflash2_verify_sample(stream, batch, block_size, vocab, draft_tokens, draft_lens, target_logits,
                                      uniforms, float(temperature), int(top_k), float(top_p), accepted, bonus,
                                      draft_prob, workspace, workspace_bytes))
+
+
+def dflash2_draft_losses_workspace_size(batch: int, block_size: int, vocab: int) -> int:
+    n = c_size_t()
+    _check(lib.dflash2_draft_losses_workspace_size(batch, block_size, vocab, ctypes.byref(n)))
+    return n.value
+
+
+def dflash2_draft_losses(handle, stream, batch, anchor_ids, labels, logits, topk_ids, topk_vals, gamma,
+                         selector_loss_weight, block_ce, selector_ce, losses, workspace, workspace_bytes) -> None:
+    _check(lib.dflash2_draft_losses(handle, stream, batch, anchor_ids, labels, logits, topk_ids, topk_vals,
+                                    float(gamma), float(selector_loss_weight), block_ce, selector_ce, losses,
+                                    workspace, workspace_bytes))

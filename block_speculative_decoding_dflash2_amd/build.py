@@ -27,9 +27,10 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-file flags: the selector must evaluate its float32 sums exactly in the
-# stated order (no fused multiply-add).
-FILE_FLAGS = {"select_verify.hip": ["-ffp-contract=off"]}
+# Per-file flags: the selector (and the selector loss, which rescores the
+# lattice) must evaluate its float32 sums exactly in the stated order (no
+# fused multiply-add).
+FILE_FLAGS = {"select_verify.hip": ["-ffp-contract=off"], "losses.hip": ["-ffp-contract=off"]}
 
 
 def _hipcc() -> str:

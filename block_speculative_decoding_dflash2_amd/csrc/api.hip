@@ -732,4 +732,54 @@ dflash2_status dflash2_verify_sample(hipStream_t stream, int32_t batch, int32_t 
   return st == DFLASH2_OK ? ok() : st;
 }
 
+dflash2_status dflash2_draft_losses_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
+                                                  size_t* bytes) {
+  if (!bytes) return fail(DFLASH2_ERR_INVALID_ARG, "draft_losses_workspace_size: null argument");
+  if (batch < 1 || block_size < 2 || vocab < 1)
+    return fail(DFLASH2_ERR_SHAPE, "draft_losses_workspace_size: bad sizes");
+  const VerifyPlan lp = plan_verify(batch, block_size - 1, vocab);
+  *bytes = align_up(size_t(batch) * (block_size - 1) * lp.nchunks * 8) + align_up(size_t(batch) * 6 * 8);
+  return ok();
+}
+
+dflash2_status dflash2_draft_losses(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                    const int32_t* anchor_ids, const int32_t* labels, const float* logits,
+                                    const int32_t* topk_ids, const float* topk_vals, float loss_decay_gamma,
+                                    float selector_loss_weight, float* block_ce, float* selector_ce,
+                                    float* losses, void* workspace, size_t workspace_bytes) {
+  if (!handle) return fail(DFLASH2_ERR_INVALID_ARG, "draft_losses: null handle");
+  const dflash2_config& c = handle->cfg;
+  if (batch < 1 || batch > c.max_batch)
+    return fail(DFLASH2_ERR_SHAPE, "draft_losses: batch %d outside 1..max_batch %d", batch, c.max_batch);
+  if (!anchor_ids || !labels || !logits || !topk_ids || !topk_vals || !losses)
+    return fail(DFLASH2_ERR_INVALID_ARG, "draft_losses: null pointer argument");
+  if (!(loss_decay_gamma > 0.0f))
+    return fail(DFLASH2_ERR_INVALID_ARG, "draft_losses: loss_decay_gamma %g is not > 0", double(loss_decay_gamma));
+  if (!std::isfinite(selector_loss_weight))
+    return fail(DFLASH2_ERR_INVALID_ARG, "draft_losses: selector_loss_weight is not finite");
+  size_t need = 0;
+  dflash2_draft_losses_workspace_size(batch, c.block_size, c.vocab, &need);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return fail(DFLASH2_ERR_WORKSPACE, "draft_losses: workspace needs %zu bytes, 256-aligned", need);
+  const int P = c.block_size - 1;
+  const VerifyPlan lp = plan_verify(batch, P, c.vocab);
+  LossArgs a{};
+  a.logits = logits; a.labels = labels; a.anchors = anchor_ids; a.ids = topk_ids; a.vals = topk_vals;
+  a.tl = handle->w.sel_tl; a.tr = handle->w.sel_tr;
+  a.B = batch; a.P = P; a.V = c.vocab; a.k = c.selector_top_k; a.r = c.selector_rank;
+  a.nchunks = lp.nchunks; a.chunk = lp.chunk;
+  a.mult = c.output_multiplier; a.cap = c.final_logit_softcapping;
+  a.gamma = loss_decay_gamma; a.sel_weight = selector_loss_weight;
+  char* ws = static_cast<char*>(workspace);
+  a.part = reinterpret_cast<float*>(ws);
+  a.seq = reinterpret_cast<double*>(ws + align_up(size_t(batch) * P * lp.nchunks * 8));
+  a.block_ce = block_ce; a.selector_ce = selector_ce; a.losses = losses;
+  const int64_t rows = int64_t(batch) * P;
+  traced(stream, DFLASH2_K_LOSS_ROWS, rows * c.vocab * 4, 0, [&] { launch_loss_rows(a, stream); });
+  traced(stream, DFLASH2_K_LOSS_SEQ, rows * (8 + int64_t(a.k) * 8 + 8) + int64_t(batch) * 4 + 16,
+         2 * rows * a.k * a.r, [&] { launch_loss_seq(a, stream); });
+  const dflash2_status st = check_launch("draft_losses");
+  return st == DFLASH2_OK ? ok() : st;
+}
+
 }  // extern "C"

@@ -160,6 +160,18 @@ struct SampleArgs {
   int32_t* kept_n; uint32_t* kept_id; uint64_t* kept_w;           // [B*bs], [B*bs][SV_OUT] x2
   int32_t* accepted; int32_t* bonus; float* draft_prob;
 };
+struct LossArgs {
+  const float* logits; const int32_t* labels; const int32_t* anchors;
+  const int32_t* ids; const float* vals; const float* tl; const float* tr;
+  int B, P, V, k, r, nchunks, chunk;
+  float mult, cap, gamma, sel_weight;
+  float* part;                    // [B*P][nchunks][2] (max, sum of exp)
+  double* seq;                    // [B][6] per-sequence sums
+  float* block_ce; float* selector_ce; float* losses;
+};
+void launch_loss_rows(const LossArgs& a, hipStream_t s);
+void launch_loss_seq(const LossArgs& a, hipStream_t s);   // per-sequence sums, then the totals
+
 // Kept sets of at most this many entries are handed from the row pass to the draw.
 constexpr int SV_OUT = 256;
 

@@ -135,7 +135,10 @@ class DFlash2:
             topk_ids = torch.empty((B, P, k), dtype=torch.int32, device=dev)
         if topk_vals is None:
             topk_vals = torch.empty((B, P, k), dtype=torch.float32, device=dev)
-        dl = torch.empty((B, P, c["vocab"]), dtype=torch.float32, device=dev) if debug_logits else None
+        if isinstance(debug_logits, torch.Tensor):
+            dl = debug_logits
+        else:
+            dl = torch.empty((B, P, c["vocab"]), dtype=torch.float32, device=dev) if debug_logits else None
         dh = torch.empty((B, P + 1, c["hidden"]), dtype=torch.float32, device=dev) if debug_hidden else None
         if workspace is None:
             workspace = self.workspace(B, max_new_rows)
@@ -161,6 +164,28 @@ class DFlash2:
                               ptr(anchors), ptr(topk_ids), ptr(topk_vals), ptr(path_idx),
                               ptr(draft_tokens), ptr(score), ptr(pair))
         return {"path": path_idx, "drafts": draft_tokens, "score": score, "pair": pair}
+
+    def draft_losses(self, anchors, labels, logits, topk_ids, topk_vals, gamma, selector_loss_weight,
+                     want_per_slot=False, workspace=None, losses=None, stream=None):
+        """Forward training losses (dflash2_draft_losses).  Returns losses [4]
+        (total, block, selector, candidate_recall) and, if asked, the
+        per-slot block and selector cross-entropies."""
+        c = self.cfg
+        B = anchors.numel()
+        P = c["block_size"] - 1
+        dev = self.device
+        if workspace is None:
+            n = L.dflash2_draft_losses_workspace_size(B, c["block_size"], c["vocab"])
+            workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+        if losses is None:
+            losses = torch.empty((4,), dtype=torch.float32, device=dev)
+        bce = torch.empty((B, P), dtype=torch.float32, device=dev) if want_per_slot else None
+        sce = torch.empty((B, P), dtype=torch.float32, device=dev) if want_per_slot else None
+        L.dflash2_draft_losses(self.handle, current_stream() if stream is None else stream, B, ptr(anchors),
+                               ptr(labels), ptr(logits), ptr(topk_ids), ptr(topk_vals), gamma,
+                               selector_loss_weight, ptr(bce), ptr(sce), ptr(losses), ptr(workspace),
+                               workspace.numel())
+        return {"losses": losses, "block_ce": bce, "selector_ce": sce}
 
     def select_path_stop(self, anchors, topk_ids, topk_vals, p_min=0.0, n_min=0, n_max=None,
                          want_conf=False, want_score=False, path_idx=None, draft_tokens=None,

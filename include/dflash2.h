@@ -302,6 +302,46 @@ dflash2_status dflash2_verify_sample(hipStream_t stream, int32_t batch, int32_t 
                                      int32_t top_k, float top_p, int32_t* accepted, int32_t* bonus,
                                      float* draft_prob, void* workspace, size_t workspace_bytes);
 
+/* Bytes of device workspace dflash2_draft_losses needs. */
+dflash2_status dflash2_draft_losses_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
+                                                  size_t* bytes);
+
+/* Training-side forward losses on given logits and labels (NeMo AutoModel
+ * page, "Objective"): slots 1..block_size-1 are supervised; slot k's
+ * cross-entropy on the transformed logits (output_multiplier, then
+ * final_logit_softcapping, as in decoding) is weighted by
+ * w_k = exp(-(k-1) / loss_decay_gamma); DFlash 2 adds, weighted by
+ * selector_loss_weight, a cross-entropy over slot k's top-k candidates
+ * scored as the lattice scores them, pi(true_{k-1}, c_kj) + topk_vals[kj]
+ * (float32, multiply then add, m ascending), against the ground-truth
+ * predecessor true_{k-1} (the anchor for k = 1, else labels[k-2]).
+ *   labels   [device] int32 [batch, block_size-1]: true token of slots
+ *            1..block_size-1; outside [0, vocab) = unsupervised (no term,
+ *            not counted).
+ *   logits   [device] float [batch, block_size-1, vocab]: the draft's
+ *            pre-transform logits (as dflash2_draft_block's debug_logits);
+ *            NaN logits give unspecified losses.
+ *   topk_ids, topk_vals as dflash2_draft_block produces them.
+ *   loss_decay_gamma > 0 (+inf: equal weights); selector_loss_weight finite;
+ *            else DFLASH2_ERR_INVALID_ARG.
+ *   block_ce    [device, nullable] float [batch, block_size-1]: CE per slot
+ *               (NaN where unsupervised).
+ *   selector_ce [device, nullable] float [batch, block_size-1]: selector CE
+ *               where the label is among the candidates and its predecessor
+ *               is known, NaN elsewhere.
+ *   losses   [device] float [4]: total = block + weight * selector, block =
+ *            sum w_k CE_k / sum w_k over supervised slots, selector = mean
+ *            selector CE over slots with a signal (0 if none),
+ *            candidate_recall = supervised slots whose label is among the
+ *            candidates / supervised slots.
+ * logsumexp runs in float32 (per-chunk online maxima and sums merged in a
+ * fixed order); the sums over slots and sequences in double, in order. */
+dflash2_status dflash2_draft_losses(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                    const int32_t* anchor_ids, const int32_t* labels, const float* logits,
+                                    const int32_t* topk_ids, const float* topk_vals, float loss_decay_gamma,
+                                    float selector_loss_weight, float* block_ce, float* selector_ce,
+                                    float* losses, void* workspace, size_t workspace_bytes);
+
 /* Optional per-kernel timing (instrumentation for benchmarks and profiling).
  * While a trace is attached on a thread, every kernel that calls from this
  * thread enqueue is bracketed by hipEventRecord(entry.start / entry.stop) on
@@ -326,7 +366,9 @@ typedef enum {
   DFLASH2_K_VERIFY_PARTIAL = 10,
   DFLASH2_K_VERIFY_FINAL = 11,
   DFLASH2_K_SAMPLE_ROWS = 12,  /* sampled verification: per-row truncation */
-  DFLASH2_K_SAMPLE_PICK = 13   /* sampled verification: accept walk + draw */
+  DFLASH2_K_SAMPLE_PICK = 13,  /* sampled verification: accept walk + draw */
+  DFLASH2_K_LOSS_ROWS = 14,    /* forward losses: per-chunk logsumexp       */
+  DFLASH2_K_LOSS_SEQ = 15      /* forward losses: per-slot terms and totals */
 } dflash2_kernel_kind;
 
 typedef struct {

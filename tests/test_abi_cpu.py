@@ -211,3 +211,35 @@ def test_verify_sample_argument_errors():
         with pytest.raises(L.DFlash2Error) as e:
             call(**kw)
         assert e.value.status == status, kw
+
+
+def test_draft_losses_argument_errors():
+    n = L.dflash2_draft_losses_workspace_size(4, 8, 1000)
+    assert n > 0 and n % 256 == 0
+    w = synth.get("small_bf16")
+    cfg = w.abi_config()
+    wts, keep = _fake_weights(cfg["num_layers"], False)
+    h = L.dflash2_create(config_struct(cfg), wts)
+    try:
+        p = 0x1000
+        nb = L.dflash2_draft_losses_workspace_size(1, cfg["block_size"], cfg["vocab"])
+
+        def call(**kw):
+            a = dict(batch=1, anchors=p, labels=p, logits=p, ids=p, vals=p, gamma=4.0, wsel=0.5, losses=p,
+                     ws=p, nbytes=nb)
+            a.update(kw)
+            L.dflash2_draft_losses(h, None, a["batch"], a["anchors"], a["labels"], a["logits"], a["ids"],
+                                   a["vals"], a["gamma"], a["wsel"], None, None, a["losses"], a["ws"],
+                                   a["nbytes"])
+
+        cases = [(dict(batch=0), L.DFLASH2_ERR_SHAPE), (dict(batch=cfg["max_batch"] + 1), L.DFLASH2_ERR_SHAPE),
+                 (dict(labels=None), L.DFLASH2_ERR_INVALID_ARG), (dict(losses=None), L.DFLASH2_ERR_INVALID_ARG),
+                 (dict(gamma=0.0), L.DFLASH2_ERR_INVALID_ARG), (dict(gamma=float("nan")), L.DFLASH2_ERR_INVALID_ARG),
+                 (dict(wsel=float("inf")), L.DFLASH2_ERR_INVALID_ARG), (dict(nbytes=nb - 8), L.DFLASH2_ERR_WORKSPACE),
+                 (dict(ws=p + 8), L.DFLASH2_ERR_WORKSPACE)]
+        for kw, status in cases:
+            with pytest.raises(L.DFlash2Error) as e:
+                call(**kw)
+            assert e.value.status == status, kw
+    finally:
+        L.dflash2_destroy(h)
