@@ -19,7 +19,7 @@ DTYPE_CODE = {"fp32": DFLASH2_FP32, "bf16": DFLASH2_BF16, "fp8": DFLASH2_FP8_E4M
 _INT_FIELDS = ("hidden", "num_layers", "num_q_heads", "num_kv_heads", "head_dim", "ffn", "vocab",
                "num_taps", "tap_width", "block_size", "conv_kernel_size", "selector_top_k",
                "selector_rank", "max_batch", "max_context", "sliding_window", "mask_token_id",
-               "weight_dtype")
+               "weight_dtype", "conv_group_size")
 _FLOAT_FIELDS = ("rms_eps", "rope_theta", "input_embedding_scale", "output_multiplier",
                  "final_logit_softcapping")
 
@@ -31,7 +31,8 @@ class dflash2_config(ctypes.Structure):
 class dflash2_layer_weights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in (
         "conv_attn", "attn_norm", "wqkv", "wqkv_scale", "wo", "wo_scale", "conv_ffn", "ffn_norm",
-        "w_gate_up", "w_gate_up_scale", "w_down", "w_down_scale")]
+        "w_gate_up", "w_gate_up_scale", "w_down", "w_down_scale", "dconv_attn", "dconv_attn_scale",
+        "dconv_ffn", "dconv_ffn_scale")]
 
 
 class dflash2_weights(ctypes.Structure):

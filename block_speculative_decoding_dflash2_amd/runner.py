@@ -16,7 +16,7 @@ from . import _lib as L
 def config_struct(cfg: Dict) -> L.dflash2_config:
     c = L.dflash2_config()
     for name in L._INT_FIELDS:
-        v = cfg[name]
+        v = cfg.get(name, 0) if name == "conv_group_size" else cfg[name]
         if name == "weight_dtype" and isinstance(v, str):
             v = L.DTYPE_CODE[v]
         setattr(c, name, int(v))
@@ -65,10 +65,13 @@ class DFlash2:
         self._layers = (L.dflash2_layer_weights * nl)()
         for i, lw in enumerate(weights.layers):
             x = self._layers[i]
-            for name in ("conv_attn", "attn_norm", "wqkv", "wo", "conv_ffn", "ffn_norm", "w_gate_up", "w_down"):
-                t = getattr(lw, name)
+            for name in ("conv_attn", "attn_norm", "wqkv", "wo", "conv_ffn", "ffn_norm", "w_gate_up", "w_down",
+                         "dconv_attn", "dconv_ffn"):
+                t = getattr(lw, name, None)
+                if t is None:
+                    continue
                 setattr(x, name, up(t.data))
-                if name in ("wqkv", "wo", "w_gate_up", "w_down"):
+                if name in ("wqkv", "wo", "w_gate_up", "w_down", "dconv_attn", "dconv_ffn"):
                     setattr(x, name + "_scale", up(t.scale))
         w = L.dflash2_weights()
         for name in ("embed", "proj_norm", "final_norm", "sel_tl", "sel_tr"):

@@ -93,6 +93,10 @@ typedef struct {
   int32_t sliding_window;   /* draft_sliding_window; 0 = attend to all rows   */
   int32_t mask_token_id;    /* reserved id filling slots 1..block_size-1      */
   int32_t weight_dtype;     /* dflash2_dtype of the linears and lm_head       */
+  int32_t conv_group_size;  /* 0: static per-channel taps (conv_attn/conv_ffn);
+                               > 0: dynamic taps, one set per group of this
+                               many channels, computed from the slot's input
+                               (dconv_attn/dconv_ffn); must divide hidden   */
   float rms_eps;            /* RMSNorm epsilon                                */
   float rope_theta;         /* RoPE base                                      */
   float input_embedding_scale;   /* scales the embedded block (1 = identity)  */
@@ -103,7 +107,8 @@ typedef struct {
 /* Per-layer weights [device].  *_scale are float32 [out rows], required for
  * FP8_E4M3 and ignored otherwise. */
 typedef struct {
-  const void* conv_attn;     /* [conv_kernel_size, H] param: tap j multiplies slot t-j */
+  const void* conv_attn;     /* [conv_kernel_size, H] param: tap j multiplies slot t-j
+                                (static taps; unused with conv_group_size > 0) */
   const void* attn_norm;     /* [H] param                                     */
   const void* wqkv;          /* [(nq + 2 nkv) * d, H]: q heads, k heads, v heads */
   const float* wqkv_scale;
@@ -115,6 +120,17 @@ typedef struct {
   const float* w_gate_up_scale;
   const void* w_down;        /* [H, F]                                        */
   const float* w_down_scale;
+  /* Dynamic convolution (conv_group_size G > 0, NeMo SpeechLM page, "DFlash2
+   * inference": DFlash2 adds dynamic convolutions; NeMo AutoModel page, "Key
+   * Config Fields": conv_group_size channels per dynamic correction).  Slot
+   * t's taps are c[t] = W x_t with W [(H/G) * conv_kernel_size, H] (weight
+   * dtype), row g * conv_kernel_size + j = tap j of channel group g, and
+   * y_t[ch] = x_t[ch] + sum_j c[t][ch / G][j] * x_{t-j}[ch].  Ignored (may be
+   * null) when conv_group_size is 0; the static conv_* are then used. */
+  const void* dconv_attn;
+  const float* dconv_attn_scale;
+  const void* dconv_ffn;
+  const float* dconv_ffn_scale;
 } dflash2_layer_weights;
 
 /* Draft weights.  Device pointers, not owned: they must outlive the handle.

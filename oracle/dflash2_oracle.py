@@ -152,6 +152,25 @@ def block_conv(x: np.ndarray, taps: np.ndarray) -> np.ndarray:
     return y
 
 
+def dynamic_block_conv(x: np.ndarray, wc, kernel: int, group: int) -> np.ndarray:
+    """In-block convolution with dynamic, group-shared taps (Readings D1-D3):
+    slot t's taps c[t] = W x_t, reshaped [H / group, kernel] (row
+    g * kernel + j of W is tap j of channel group g), and
+    y[t, ch] = x[t, ch] + sum_{j<kernel} c[t, ch // group, j] * x[t-j, ch],
+    with x[t-j] = 0 before slot 0.  [VL §DFlash2 inference: DFlash2 adds
+    dynamic convolutions; AM §Key Config Fields: conv_kernel_size taps and
+    conv_group_size channels per dynamic correction; AM §Variants: the
+    convolution stays inside the block.]  x [bs, H] float64; wc a stored
+    weight Tensor [(H / group) * kernel, H]."""
+    bs, H = x.shape
+    taps = linear(x, wc).reshape(bs, H // group, kernel)
+    per_channel = np.repeat(taps, group, axis=1)          # [bs, H, kernel]
+    y = x.copy()
+    for j in range(kernel):
+        y[j:] += per_channel[j:, :, j] * x[:bs - j]
+    return y
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     """Unmasked (non-causal) softmax attention with grouped KV heads.
     q [T, nq, d], k/v [S, nkv, d] -> [T, nq, d].  q-head i reads kv head
@@ -265,9 +284,16 @@ def draft_block(w, W, k_cache, v_cache, anchors, ctx_lens) -> Dict[str, np.ndarr
     h = np.stack([w.input_embedding_scale * decode_rows(E, int(t), int(t) + 1)[0]
                   for t in tokens.reshape(-1)]).reshape(B, bs, H)
     pos = np.asarray(ctx_lens, dtype=np.int64)[:, None] + np.arange(bs)[None, :]
+    G = getattr(w, "conv_group_size", 0)
+
+    def conv(x, static, dyn):
+        if G > 0:
+            return np.stack([dynamic_block_conv(x[b], dyn, w.conv_kernel_size, G) for b in range(B)])
+        taps = decode(static)
+        return np.stack([block_conv(x[b], taps) for b in range(B)])
+
     for l, layer in enumerate(W.layers):
-        ca, cf = decode(layer.conv_attn), decode(layer.conv_ffn)
-        h = np.stack([block_conv(h[b], ca) for b in range(B)])
+        h = conv(h, layer.conv_attn, layer.dconv_attn)
         n = rmsnorm(h, decode(layer.attn_norm), w.rms_eps)
         qkv = linear(n, layer.wqkv)                       # [B, bs, (nq+2nkv)d]
         o = np.empty((B, bs, nq * d))
@@ -281,7 +307,7 @@ def draft_block(w, W, k_cache, v_cache, anchors, ctx_lens) -> Dict[str, np.ndarr
             vc = v_cache[l, b, :, lo:L, :].transpose(1, 0, 2)
             o[b] = attention(q, np.concatenate([kc, kb]), np.concatenate([vc, vb])).reshape(bs, nq * d)
         h = h + linear(o, layer.wo)
-        h = np.stack([block_conv(h[b], cf) for b in range(B)])
+        h = conv(h, layer.conv_ffn, layer.dconv_ffn)
         n = rmsnorm(h, decode(layer.ffn_norm), w.rms_eps)
         gu = linear(n, layer.w_gate_up)
         act = silu(gu[..., :w.ffn]) * gu[..., w.ffn:]

@@ -40,6 +40,7 @@ class Workload:
     agree: Tuple[str, float]     # ("const", p) or ("decay", p0): p_k = p0 * exp(-(k-1)/gamma)
     decay_gamma: float = 7.0
     conv_kernel_size: int = 2
+    conv_group_size: int = 0     # 0: static per-channel taps; > 0: dynamic taps per channel group
     cold: bool = False           # cache empty before the step: n_new = ctx (whole context appended)
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
@@ -85,6 +86,7 @@ class Workload:
             num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, ffn=self.ffn,
             vocab=self.vocab, num_taps=self.num_taps, tap_width=self.tap_width,
             block_size=self.block_size, conv_kernel_size=self.conv_kernel_size,
+            conv_group_size=self.conv_group_size,
             selector_top_k=self.top_k, selector_rank=self.rank, max_batch=self.batch,
             max_context=self.max_context, sliding_window=self.sliding_window,
             mask_token_id=self.mask_token_id, weight_dtype=self.weight_dtype,

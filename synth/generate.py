@@ -28,7 +28,7 @@ CHUNK = 1 << 22
 
 # tensor ids (seed components)
 T_EMBED, T_LMHEAD, T_PROJ, T_PROJ_NORM, T_FINAL_NORM, T_SEL_L, T_SEL_R = range(7)
-L_CONV_ATTN, L_ATTN_NORM, L_WQKV, L_WO, L_CONV_FFN, L_FFN_NORM, L_WGU, L_WDOWN = range(8)
+L_CONV_ATTN, L_ATTN_NORM, L_WQKV, L_WO, L_CONV_FFN, L_FFN_NORM, L_WGU, L_WDOWN, L_DCONV_ATTN, L_DCONV_FFN = range(10)
 S_ANCHOR, S_CTXLEN, S_ACCEPT, S_TAPS, S_KCACHE, S_VCACHE = range(1000, 1006)
 S_VERIFIED_TAPS = 1006
 V_LOGITS, V_PLANT = 2000, 2001
@@ -134,6 +134,8 @@ class Layer:
     ffn_norm: Tensor    # [H]
     w_gate_up: Tensor   # [2F, H]  rows 0..F-1 gate, F..2F-1 up
     w_down: Tensor      # [H, F]
+    dconv_attn: Optional[Tensor] = None   # [(H / G) K, H] weight dtype (dynamic taps, G = conv_group_size)
+    dconv_ffn: Optional[Tensor] = None
 
 
 @dataclasses.dataclass
@@ -172,6 +174,10 @@ def make_weights(w: Workload) -> Weights:
             w_gate_up=encode(normal((2 * w.ffn, H), t(L_WGU), sd), wd),
             w_down=encode(normal((H, w.ffn), t(L_WDOWN), sd), wd),
         ))
+        if w.conv_group_size > 0:
+            gk = H // w.conv_group_size * w.conv_kernel_size
+            layers[-1].dconv_attn = encode(normal((gk, H), t(L_DCONV_ATTN), sd), wd)
+            layers[-1].dconv_ffn = encode(normal((gk, H), t(L_DCONV_FFN), sd), wd)
     tl, tr = make_selector_tables(w)
     return Weights(
         embed=encode(normal((V, H), (w.index, T_EMBED), sd), pd),

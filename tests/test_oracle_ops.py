@@ -10,6 +10,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle as O
+import synth
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -120,3 +121,40 @@ def test_logit_transform():
     assert np.all(np.abs(y) < 10.0) and np.allclose(y, -O.logit_transform(-x, 0.5, 10.0))
     assert np.all(np.diff(y) > 0)
     assert np.isclose(O.logit_transform(np.array([1e-4]), 0.5, 10.0)[0], 0.5e-4, rtol=1e-8)
+
+
+# ------------------------------------------------- dynamic convolution
+
+def _fp32_tensor(a):
+    return synth.Tensor(np.asarray(a, dtype=np.float32), "fp32")
+
+
+def test_dynamic_conv_hand_case():
+    """H = 2, one channel per group, two taps: row g*K + j of W is tap j of
+    group g.  W picks x_t[0] as group 0's own-slot tap and x_t[1] as group
+    1's previous-slot tap."""
+    x = np.array([[1.0, 2.0], [3.0, 4.0]])
+    W = _fp32_tensor([[1, 0], [0, 0], [0, 0], [0, 1]])
+    y = O.dynamic_block_conv(x, W, kernel=2, group=1)
+    np.testing.assert_array_equal(y, [[2.0, 2.0], [12.0, 12.0]])
+
+
+def test_dynamic_conv_taps_are_shared_by_a_group():
+    x = np.array([[1.0, 1.0, 2.0, 3.0]])
+    W = np.zeros((4, 4), dtype=np.float32)
+    W[2, 2] = 1.0                        # group 1 (channels 2, 3), tap 0 = x_t[2]
+    y = O.dynamic_block_conv(x, _fp32_tensor(W), kernel=2, group=2)
+    np.testing.assert_array_equal(y, [[1.0, 1.0, 6.0, 9.0]])
+
+
+def test_dynamic_conv_identity_and_causality():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 8))
+    assert np.array_equal(O.dynamic_block_conv(x, _fp32_tensor(np.zeros((12, 8))), 3, 2), x)
+    W = _fp32_tensor(rng.standard_normal((12, 8)) * 0.1)
+    y = O.dynamic_block_conv(x, W, 3, 2)
+    x2 = x.copy()
+    x2[3] += 1.0                          # a later slot never reaches back
+    y2 = O.dynamic_block_conv(x2, W, 3, 2)
+    np.testing.assert_array_equal(y[:3], y2[:3])
+    assert not np.allclose(y[3:], y2[3:])
