@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--losses", default=None, metavar="GAMMA,WEIGHT",
                     help="also evaluate the forward training losses on the step's logits (the draft "
                          "then writes its float32 logits) with synthetic labels")
+    ap.add_argument("--conv-group-size", type=int, default=None,
+                    help="run the workload with dynamic grouped convolution (channels per group)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -100,6 +102,8 @@ def main():
     from block_speculative_decoding_dflash2_amd.metrics import speculative_metrics
 
     w = synth.get(args.workload)
+    if args.conv_group_size:
+        w = w.replace(conv_group_size=args.conv_group_size)
     t0 = time.time()
     W = synth.make_weights(w)
     inp = synth.make_step_inputs(w)
@@ -264,7 +268,9 @@ def main():
                    "vocab": V, "top_k": k, "selector_rank": w.rank, "parallelism": "none (1 GPU)",
                    "verification": ("greedy" if sampling is None else
                                     "rejection sampling T=%g top_k=%d top_p=%g" % sampling),
-                   "draft_p_min": args.p_min, "forward_losses": args.losses},
+                   "draft_p_min": args.p_min, "forward_losses": args.losses,
+                   "conv": (f"dynamic, {w.conv_group_size} channels per group" if w.conv_group_size
+                            else "static per-channel taps")},
         "draft_tokens_per_s": round(B * (bs - 1) / s_step, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

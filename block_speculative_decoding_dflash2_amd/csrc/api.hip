@@ -143,11 +143,11 @@ AttnPlan plan_attn(const dflash2_config& c, int B) {
 
 struct Plan {
   int B, M, Mh, Mn;
-  Split proj, kv, qkv, o, gu, down;
+  Split proj, kv, qkv, o, gu, down, dconv;
   AttnPlan attn;
   int groups;
   size_t off_h0, off_h1, off_n, off_sumsq, off_q, off_o, off_a, off_parts, off_attn_o, off_attn_ml,
-      off_cand;
+      off_cand, off_hpre;
   size_t total;
 };
 
@@ -165,6 +165,8 @@ Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
   p.o = plan_split(dt, p.M, H, qd);
   p.gu = plan_split(dt, p.M, 2 * F, H);
   p.down = plan_split(dt, p.M, H, F);
+  const int gk = c.conv_group_size > 0 ? H / c.conv_group_size * c.conv_kernel_size : 0;
+  p.dconv = gk > 0 ? plan_split(dt, p.M, gk, H) : Split{1, H};
   p.attn = plan_attn(c, B);
   p.groups = int(cdiv(c.vocab, 256));
   const size_t ab = act_bytes(c);
@@ -178,6 +180,7 @@ Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
   upd(size_t(p.o.splits) * p.M * H);
   upd(size_t(p.gu.splits) * p.M * 2 * F);
   upd(size_t(p.down.splits) * p.M * H);
+  if (gk > 0) upd(size_t(p.dconv.splits) * p.M * gk);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -198,6 +201,8 @@ Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
   // candidate lists: the weight-streaming lm_head writes groups x k keys per
   // row, the tiled one at most groups lists of 16
   p.off_cand = take(size_t(p.Mh) * p.groups * std::max(c.selector_top_k, 16) * 8);
+  // dynamic convolution: each conv site's input rows, float32
+  p.off_hpre = gk > 0 ? take(size_t(p.M) * H * 4) : 0;
   p.total = off;
   return p;
 }
@@ -253,6 +258,9 @@ dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weight
   if (c.conv_kernel_size < 1 || c.conv_kernel_size > c.block_size)
     return fail(DFLASH2_ERR_SHAPE, "create: conv_kernel_size %d outside 1..block_size",
                 c.conv_kernel_size);
+  if (c.conv_group_size < 0 || (c.conv_group_size > 0 && c.hidden % c.conv_group_size))
+    return fail(DFLASH2_ERR_SHAPE, "create: conv_group_size %d must be 0 or divide hidden %d",
+                c.conv_group_size, c.hidden);
   if (c.selector_top_k < 1 || c.selector_top_k > 64 || c.selector_top_k > c.vocab)
     return fail(DFLASH2_ERR_SHAPE, "create: selector_top_k %d outside 1..min(64, vocab)",
                 c.selector_top_k);
@@ -285,10 +293,12 @@ dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weight
     return fail(DFLASH2_ERR_INVALID_ARG, "create: fp8 weights need scales");
   for (int l = 0; l < c.num_layers; ++l) {
     const dflash2_layer_weights& L = w.layers[l];
-    if (!L.conv_attn || !L.attn_norm || !L.wqkv || !L.wo || !L.conv_ffn || !L.ffn_norm ||
-        !L.w_gate_up || !L.w_down)
+    const bool dyn = c.conv_group_size > 0;
+    if (!L.attn_norm || !L.wqkv || !L.wo || !L.ffn_norm || !L.w_gate_up || !L.w_down ||
+        (!dyn && (!L.conv_attn || !L.conv_ffn)) || (dyn && (!L.dconv_attn || !L.dconv_ffn)))
       return fail(DFLASH2_ERR_INVALID_ARG, "create: null weight pointer in layer %d", l);
-    if (fp8 && (!L.wqkv_scale || !L.wo_scale || !L.w_gate_up_scale || !L.w_down_scale))
+    if (fp8 && (!L.wqkv_scale || !L.wo_scale || !L.w_gate_up_scale || !L.w_down_scale ||
+                (dyn && (!L.dconv_attn_scale || !L.dconv_ffn_scale))))
       return fail(DFLASH2_ERR_INVALID_ARG, "create: fp8 weights need scales (layer %d)", l);
   }
   dflash2_handle* h = new dflash2_handle;
@@ -373,19 +383,42 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
     traced(stream, DFLASH2_K_GEMM, bytes, 2 * int64_t(M) * N * K, [&] { launch_gemm(dt, a, stream); });
     return fused;
   };
+  const int G = c.conv_group_size;
+  const int GK = G > 0 ? H / G * c.conv_kernel_size : 0;
+  float* hpre = G > 0 ? reinterpret_cast<float*>(ws + P.off_hpre) : nullptr;
   auto norm = [&](int rows, const int32_t* rows_dev, int nbs, const void* embed, const float* base,
                   const float* prt, const Split* sp, int64_t pstride, const void* conv,
-                  const void* gain, float* h_out, void* n_out, int t_first) {
+                  const void* gain, float* h_out, void* n_out, int t_first, const float* dtaps = nullptr) {
     NormArgs a{};
+    if (dtaps) {
+      a.dtaps = dtaps; a.dsplits = P.dconv.splits; a.dstride = int64_t(rows) * GK; a.dgk = GK; a.dgroup = G;
+    }
     a.H = H; a.rows = rows; a.rows_dev = rows_dev; a.bs = nbs;
     a.embed = embed; a.anchors = anchor_ids; a.mask_id = c.mask_token_id; a.vocab = c.vocab;
     a.emb_scale = c.input_embedding_scale;
     a.base = base; a.parts = prt; a.splits = sp ? sp->splits : 0; a.split_stride = pstride; a.ldp = H;
     a.conv = conv; a.conv_k = c.conv_kernel_size; a.gain = gain;
     a.h_out = h_out; a.n_out = n_out; a.sumsq = sumsq; a.t_first = t_first;
-    const int64_t in_rows = int64_t(rows) * H * ((embed ? ab : 0) + (base ? 4 : 0) + 4 * a.splits);
+    const int64_t in_rows = int64_t(rows) * H * ((embed ? ab : 0) + (base ? 4 : 0) + 4 * a.splits) +
+                            (dtaps ? int64_t(rows) * GK * 4 * a.dsplits : 0);
     const int64_t out_rows = int64_t(rows) * H * ((h_out ? 4 : 0) + ab);
     traced(stream, DFLASH2_K_NORM, in_rows + out_rows, 0, [&] { launch_norm(f32, a, stream); });
+  };
+
+  // Residual update + in-block convolution + RMSNorm of the block rows.  With
+  // dynamic taps (conv_group_size > 0) the conv input is materialised first
+  // (float32 for the conv, the activation dtype for the tap GEMM), the taps of
+  // every slot are one GEMM against W_dconv, and the conv pass reads them.
+  auto conv_norm = [&](const void* embed, const float* base, const float* prt, const Split* sp,
+                       int64_t pstride, const void* conv, const void* dconv, const float* dscale,
+                       const void* gain, float* h_out) {
+    if (G == 0) {
+      norm(P.M, nullptr, bs, embed, base, prt, sp, pstride, conv, gain, h_out, nbuf, 0);
+      return;
+    }
+    norm(P.M, nullptr, bs, embed, base, prt, sp, pstride, nullptr, nullptr, hpre, nbuf, 0);
+    gemm(nbuf, H, dconv, dscale, P.M, nullptr, GK, H, P.dconv, parts, plain);
+    norm(P.M, nullptr, bs, nullptr, hpre, nullptr, nullptr, 0, nullptr, gain, h_out, nbuf, 0, parts);
   };
 
   // ---- 1. context append -------------------------------------------------
@@ -430,8 +463,8 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
 
   // ---- 2. block forward --------------------------------------------------
   const dflash2_layer_weights& L0 = handle->layers[0];
-  norm(P.M, nullptr, bs, handle->w.embed, nullptr, nullptr, nullptr, 0, L0.conv_attn, L0.attn_norm,
-       h0, nbuf, 0);
+  conv_norm(handle->w.embed, nullptr, nullptr, nullptr, 0, L0.conv_attn, L0.dconv_attn,
+            dt == DFLASH2_FP8_E4M3 ? L0.dconv_attn_scale : nullptr, L0.attn_norm, h0);
   for (int l = 0; l < c.num_layers; ++l) {
     const dflash2_layer_weights& L = handle->layers[l];
     const bool fp8 = dt == DFLASH2_FP8_E4M3;
@@ -471,8 +504,8 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
            [&] { launch_attn_combine(f32, ca, stream); });
 
     gemm(obuf, qd, L.wo, fp8 ? L.wo_scale : nullptr, P.M, nullptr, H, qd, P.o, parts, plain);
-    norm(P.M, nullptr, bs, nullptr, h0, parts, &P.o, int64_t(P.M) * H, L.conv_ffn, L.ffn_norm, h1,
-         nbuf, 0);
+    conv_norm(nullptr, h0, parts, &P.o, int64_t(P.M) * H, L.conv_ffn, L.dconv_ffn,
+              fp8 ? L.dconv_ffn_scale : nullptr, L.ffn_norm, h1);
     GemmEpi se{};
     se.kind = EPI_SWIGLU;
     se.act_out = abuf; se.F = F;
@@ -487,8 +520,8 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
     gemm(abuf, F, L.w_down, fp8 ? L.w_down_scale : nullptr, P.M, nullptr, H, F, P.down, parts, plain);
     if (l + 1 < c.num_layers) {
       const dflash2_layer_weights& Ln = handle->layers[l + 1];
-      norm(P.M, nullptr, bs, nullptr, h1, parts, &P.down, int64_t(P.M) * H, Ln.conv_attn,
-           Ln.attn_norm, h0, nbuf, 0);
+      conv_norm(nullptr, h1, parts, &P.down, int64_t(P.M) * H, Ln.conv_attn, Ln.dconv_attn,
+                fp8 ? Ln.dconv_attn_scale : nullptr, Ln.attn_norm, h0);
     } else {
       norm(P.M, nullptr, bs, nullptr, h1, parts, &P.down, int64_t(P.M) * H, nullptr,
            handle->w.final_norm, debug_hidden, nbuf, 1);

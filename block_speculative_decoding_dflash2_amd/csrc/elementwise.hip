@@ -39,6 +39,8 @@ __device__ __forceinline__ float sum_parts(const float* __restrict__ parts, int 
 //   input  h_in[r] = emb_scale * E[token]           (embedding mode)
 //                  = base[r] + sum_s parts[s][r]      (residual mode)
 //   conv   y[r]    = h_in[r] + sum_{j < conv_k, t - j >= 0} conv[j] * h_in[r - j]
+//          (dynamic: conv[j] -> the slot's own tap j of the channel's group,
+//          summed from the tap GEMM's split-K partials)
 //   outputs h_out[r] = y[r];  n_out[o] = gain * y[r];  sumsq[o][col block] = sum y^2
 // for output row o = b * (bs - t_first) + t - t_first when t >= t_first.
 // The RMSNorm factor 1/rms(y) is one scalar per row, so the consuming GEMM
@@ -76,12 +78,22 @@ __global__ __launch_bounds__(256) void resconv_kernel(NormArgs p) {
       const float x0 = y;
       y = x0 + Act<T>::load(C, c) * x0;
       for (int j = 1; j < p.conv_k && t - j >= 0; ++j) y += Act<T>::load(C, int64_t(j) * H + c) * hin(r - j);
+    } else if (p.dtaps) {
+      // dynamic taps of this slot, shared by the channel group of c
+      const int64_t trow = int64_t(r) * p.dgk + int64_t(c / p.dgroup) * p.conv_k;
+      const float x0 = y;
+      y = x0 + sum_parts(p.dtaps, p.dsplits, p.dstride, trow) * x0;
+      for (int j = 1; j < p.conv_k && t - j >= 0; ++j)
+        y += sum_parts(p.dtaps, p.dsplits, p.dstride, trow + j) * hin(r - j);
     }
     if (p.h_out) p.h_out[int64_t(r) * H + c] = y;
   }
   if (t < p.t_first) return;  // uniform per block
   const int orow = b * (p.bs - p.t_first) + (t - p.t_first);
-  if (c < H) Act<T>::store(static_cast<T*>(p.n_out), int64_t(orow) * H + c, y * Act<T>::load(static_cast<const T*>(p.gain), c));
+  if (c < H) {
+    const float g = p.gain ? Act<T>::load(static_cast<const T*>(p.gain), c) : 1.0f;
+    Act<T>::store(static_cast<T*>(p.n_out), int64_t(orow) * H + c, y * g);
+  }
   const float ss = block_sum(y * y, red);
   if (threadIdx.x == 0) p.sumsq[int64_t(orow) * gridDim.y + blockIdx.y] = ss;
 }

@@ -81,7 +81,10 @@ struct NormArgs {
   const float* base;              // [rows][H] or null
   const float* parts; int splits; int64_t split_stride; int64_t ldp;  // partial sums
   const void* conv; int conv_k;   // [conv_k][H] param or null
-  const void* gain;
+  // dynamic taps (conv == null): split-K partial sums of [rows][dgk] taps,
+  // tap j of channel c at column (c / dgroup) * conv_k + j; null = none
+  const float* dtaps; int dsplits; int64_t dstride; int dgk; int dgroup;
+  const void* gain;               // null: n_out = y (no gain)
   float* h_out;                   // [rows][H] float32 or null
   void* n_out;                    // act [out rows][H]: gain * y; row map below
   float* sumsq;                   // [out rows][col_blocks] sums of y^2

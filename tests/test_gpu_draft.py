@@ -248,3 +248,18 @@ def test_draft_sliding_window(name, window):
         check_step(g, res, range(w.batch))
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name,group", [("tiny_fp32", 16), ("small_fp32", 32), ("small_bf16", 32),
+                                        ("small_fp8", 64), ("medium_bf16", 16), ("medium_fp8", 320)])
+def test_draft_dynamic_conv(name, group):
+    """Dynamic grouped convolution (conv_group_size > 0): every conv site's
+    taps come from a GEMM against W_dconv on the slot's input; appended
+    cache rows, hidden states and logits within the dtype bound."""
+    w = synth.get(name).replace(conv_group_size=group)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
