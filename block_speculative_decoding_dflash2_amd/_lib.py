@@ -58,6 +58,14 @@ class DFlash2Error(RuntimeError):
 
 
 def _load():
+    # One HIP runtime per process: the library takes device pointers and
+    # streams from PyTorch, so its libamdhip64 dependency must resolve to the
+    # runtime PyTorch loads.  Importing torch first makes the loader reuse it;
+    # loading the library first would bring in a second, separate runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "

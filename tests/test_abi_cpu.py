@@ -243,3 +243,18 @@ def test_draft_losses_argument_errors():
             assert e.value.status == status, kw
     finally:
         L.dflash2_destroy(h)
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the binding before anything else must not bring in a second
+    HIP runtime beside PyTorch's: the library receives PyTorch's device
+    pointers and streams."""
+    import subprocess
+    import sys
+    code = ("from block_speculative_decoding_dflash2_amd import _lib\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
