@@ -64,6 +64,7 @@ void traced(hipStream_t s, int kind, int64_t bytes, int64_t flops, F&& launch) {
 // Plans are a pure function of the shapes (not of the device), so results
 // and workspace sizes do not depend on which GPU runs them.
 constexpr int kTargetBlocks = 512;  // 2 blocks of 4 waves per CU on 256 CUs
+constexpr int kStreamBlockOverhead = 256;  // fixed cost of one weight-streaming block, in k
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -111,10 +112,27 @@ Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
   const int64_t blocks = cdiv(N, gemm_rows_per_block(dtype, M)) * cdiv(M, mtile) * groups;
   int S = 1;
   if (M <= 64) {
-    S = int(cdiv(kTargetBlocks, blocks));
-    S = std::min(S, std::max(1, K / 256));
-    S = std::min(S, 64);
-    S = std::max(S, 1);
+    // weight streaming: the shortest makespan over waves of kTargetBlocks
+    // resident blocks, each costing its k range plus a fixed prologue /
+    // epilogue of about kStreamBlockOverhead k; ties go to fewer splits.
+    // (Rounding the split count up to fill the slots made grids of 520-560
+    // blocks, whose second wave of 8-48 blocks doubled the kernel's time.)
+    int overhead = kStreamBlockOverhead;
+    if (const char* env = std::getenv("DFLASH2_STREAM_BLOCK_OVERHEAD")) {
+      const int v = std::atoi(env);
+      if (v >= 0 && v <= 65536) overhead = v;
+    }
+    const int max_s = std::max(1, std::min(64, K / 256));
+    double best_cost = 1e300;
+    for (int c = 1; c <= max_s; ++c) {
+      const int64_t ks = cdiv(cdiv(K, c), 32) * 32;
+      if (cdiv(K, ks) != c) continue;
+      const double cost = double(cdiv(blocks * c, kTargetBlocks)) * double(ks + overhead);
+      if (cost < best_cost * 0.999) {
+        best_cost = cost;
+        S = c;
+      }
+    }
   }
   s.k_split = int(cdiv(cdiv(K, S), 32) * 32);
   s.splits = int(cdiv(K, s.k_split));

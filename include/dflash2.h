@@ -40,7 +40,10 @@
  *     more than 64 rows (default: chosen from the shapes), and
  *     DFLASH2_TILED_MAX_SPLITS (1..16), read by dflash2_workspace_size and
  *     dflash2_draft_block, caps the K splits of those batches' linears (one
- *     split lets the GEMM apply SwiGLU and the QKV RoPE itself).  Results
+ *     split lets the GEMM apply SwiGLU and the QKV RoPE itself), and
+ *     DFLASH2_STREAM_BLOCK_OVERHEAD (0..65536, default 256), read by the same
+ *     calls, is the fixed cost of one weight-streaming block (batches of at
+ *     most 64 rows), in k, in the model that picks their K splits.  Results
  *     agree to rounding either way.
  *   - Every call returns DFLASH2_OK or an error code; on error nothing was
  *     enqueued and dflash2_last_error() (thread-local) describes it.  Device
