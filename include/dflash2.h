@@ -38,8 +38,9 @@
  *     (1..64), read at each dflash2_draft_block call, sets how many
  *     256-id vocabulary tiles one lm_head block sweeps when the batch has
  *     more than 64 rows (default: chosen from the shapes), and
- *     DFLASH2_TILED_MAX_SPLITS (1..16), read by dflash2_workspace_size and
- *     dflash2_draft_block, caps the K splits of those batches' linears (one
+ *     DFLASH2_TILED_MAX_SPLITS (1..16, default 8), read by
+ *     dflash2_workspace_size and dflash2_draft_block, caps the K splits of
+ *     those batches' linears (one
  *     split lets the GEMM apply SwiGLU and the QKV RoPE itself), and
  *     DFLASH2_STREAM_BLOCK_OVERHEAD (0..65536, default 256), read by the same
  *     calls, is the fixed cost of one weight-streaming block (batches of at
