@@ -34,68 +34,150 @@ __device__ __forceinline__ float sum_parts(const float* __restrict__ parts, int 
   return v;
 }
 
-// grid = (rows, ceil(H / 256)), one thread per (row, column).  Row r is slot
-// t = r % bs of block b = r / bs.
+// Four consecutive elements of an activation row (16 or 8 bytes, aligned:
+// every row length here is a multiple of 32).
+template <typename T> struct Act4;
+template <> struct Act4<float> {
+  __device__ static f32x4 load(const float* p, int64_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
+  __device__ static void store(float* p, int64_t i, f32x4 v) { *reinterpret_cast<f32x4*>(p + i) = v; }
+};
+template <> struct Act4<bf16_t> {
+  __device__ static f32x4 load(const bf16_t* p, int64_t i) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+    return f32x4{bf16_to_f32(bf16_t(u.x & 0xFFFFu)), bf16_to_f32(bf16_t(u.x >> 16)),
+                 bf16_to_f32(bf16_t(u.y & 0xFFFFu)), bf16_to_f32(bf16_t(u.y >> 16))};
+  }
+  __device__ static void store(bf16_t* p, int64_t i, f32x4 v) {
+    uint2 u;
+    u.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+    u.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<uint2*>(p + i) = u;
+  }
+};
+
+// sum_parts for four consecutive elements (16-byte loads, four splits in
+// flight, splits added in order).
+__device__ __forceinline__ f32x4 sum_parts4(const float* __restrict__ parts, int splits, int64_t ss,
+                                            int64_t idx) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= splits; s += 4) {
+    f32x4 t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = *reinterpret_cast<const f32x4*>(parts + (s + u) * ss + idx);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v += t[u];
+  }
+  for (; s < splits; ++s) v += *reinterpret_cast<const f32x4*>(parts + s * ss + idx);
+  return v;
+}
+
+// VEC consecutive elements (VEC = 1 or 4) of an activation / float row.
+__host__ __device__ inline int norm_col_blocks_dev(int H) { return (H + 255) / 256; }
+
+template <typename T, int VEC> struct Vec;
+template <typename T> struct Vec<T, 4> {
+  typedef f32x4 V;
+  __device__ static V act(const T* p, int64_t i) { return Act4<T>::load(p, i); }
+  __device__ static void put(T* p, int64_t i, V v) { Act4<T>::store(p, i, v); }
+  __device__ static V f32(const float* p, int64_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
+  __device__ static void putf(float* p, int64_t i, V v) { *reinterpret_cast<f32x4*>(p + i) = v; }
+  __device__ static V parts(const float* p, int s, int64_t ss, int64_t i) { return sum_parts4(p, s, ss, i); }
+  __device__ static V splat(float x) { return f32x4{x, x, x, x}; }
+  __device__ static float sq(V y) { return ((y[0] * y[0] + y[1] * y[1]) + y[2] * y[2]) + y[3] * y[3]; }
+};
+template <typename T> struct Vec<T, 1> {
+  typedef f32x1 V;
+  __device__ static V act(const T* p, int64_t i) { return V{Act<T>::load(p, i)}; }
+  __device__ static void put(T* p, int64_t i, V v) { Act<T>::store(p, i, v[0]); }
+  __device__ static V f32(const float* p, int64_t i) { return V{p[i]}; }
+  __device__ static void putf(float* p, int64_t i, V v) { p[i] = v[0]; }
+  __device__ static V parts(const float* p, int s, int64_t ss, int64_t i) { return V{sum_parts(p, s, ss, i)}; }
+  __device__ static V splat(float x) { return V{x}; }
+  __device__ static float sq(V y) { return y[0] * y[0]; }
+};
+
+// block = 256 threads, VEC consecutive columns per thread: grid = (rows,
+// ceil(H / (256 VEC))).  One element per thread for few rows, where latency
+// rules; four for many rows, where bandwidth does (a wave then covers one
+// 256-column block of the sums of squares).  Row r is slot t = r % bs of
+// block b = r / bs.
 //   input  h_in[r] = emb_scale * E[token]           (embedding mode)
 //                  = base[r] + sum_s parts[s][r]      (residual mode)
 //   conv   y[r]    = h_in[r] + sum_{j < conv_k, t - j >= 0} conv[j] * h_in[r - j]
 //          (dynamic: conv[j] -> the slot's own tap j of the channel's group,
 //          summed from the tap GEMM's split-K partials)
 //   outputs h_out[r] = y[r];  n_out[o] = gain * y[r];  sumsq[o][col block] = sum y^2
-// for output row o = b * (bs - t_first) + t - t_first when t >= t_first.
+// for output row o = b * (bs - t_first) + t - t_first when t >= t_first, one
+// sum of squares per 256 columns.
 // The RMSNorm factor 1/rms(y) is one scalar per row, so the consuming GEMM
 // applies it to its result (GemmArgs.rs); n_out * W^T * (1/rms) equals
 // RMSNorm(y) * W^T.  The in-block convolution is the DFlash 2 addition of the
 // NeMo AutoModel page ("Variants" table); RMSNorm is the draft's norm.
-template <typename T>
+template <typename T, int VEC>
 __global__ __launch_bounds__(256) void resconv_kernel(NormArgs p) {
+  typedef Vec<T, VEC> X;
+  typedef typename X::V V;
   __shared__ float red[16];
   const int rows = p.rows_dev ? min(*p.rows_dev, p.rows) : p.rows;
   const int r = blockIdx.x;
   if (r >= rows) return;
   const int t = r % p.bs, b = r / p.bs;
   const int H = p.H;
-  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * VEC;
   const T* E = static_cast<const T*>(p.embed);
   const T* C = static_cast<const T*>(p.conv);
 
-  auto hin = [&](int rr) -> float {
+  auto hin = [&](int rr) -> V {
     if (E) {
       const int tt = rr % p.bs;
       const int tok = tt == 0 ? p.anchors[rr / p.bs] : p.mask_id;
-      if (tok < 0 || tok >= p.vocab) return 0.f;
-      return p.emb_scale * Act<T>::load(E, int64_t(tok) * H + c);
+      if (tok < 0 || tok >= p.vocab) return X::splat(0.f);
+      return p.emb_scale * X::act(E, int64_t(tok) * H + c);
     }
-    float v = p.base ? p.base[int64_t(rr) * H + c] : 0.f;
-    if (p.parts) v += sum_parts(p.parts, p.splits, p.split_stride, int64_t(rr) * p.ldp + c);
+    V v = p.base ? X::f32(p.base, int64_t(rr) * H + c) : X::splat(0.f);
+    if (p.parts) v += X::parts(p.parts, p.splits, p.split_stride, int64_t(rr) * p.ldp + c);
     return v;
   };
 
-  float y = 0.f;
+  V y = X::splat(0.f);
   if (c < H) {
     y = hin(r);
     if (C) {
-      const float x0 = y;
-      y = x0 + Act<T>::load(C, c) * x0;
-      for (int j = 1; j < p.conv_k && t - j >= 0; ++j) y += Act<T>::load(C, int64_t(j) * H + c) * hin(r - j);
+      const V x0 = y;
+      y = x0 + X::act(C, c) * x0;
+      for (int j = 1; j < p.conv_k && t - j >= 0; ++j) y += X::act(C, int64_t(j) * H + c) * hin(r - j);
     } else if (p.dtaps) {
-      // dynamic taps of this slot, shared by the channel group of c
-      const int64_t trow = int64_t(r) * p.dgk + int64_t(c / p.dgroup) * p.conv_k;
-      const float x0 = y;
-      y = x0 + sum_parts(p.dtaps, p.dsplits, p.dstride, trow) * x0;
-      for (int j = 1; j < p.conv_k && t - j >= 0; ++j)
-        y += sum_parts(p.dtaps, p.dsplits, p.dstride, trow + j) * hin(r - j);
+      // dynamic taps of this slot, shared by each channel's group
+      int64_t trow[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) trow[e] = int64_t(r) * p.dgk + int64_t((c + e) / p.dgroup) * p.conv_k;
+      const V x0 = y;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[e] = x0[e] + sum_parts(p.dtaps, p.dsplits, p.dstride, trow[e]) * x0[e];
+      for (int j = 1; j < p.conv_k && t - j >= 0; ++j) {
+        const V xj = hin(r - j);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) y[e] += sum_parts(p.dtaps, p.dsplits, p.dstride, trow[e] + j) * xj[e];
+      }
     }
-    if (p.h_out) p.h_out[int64_t(r) * H + c] = y;
+    if (p.h_out) X::putf(p.h_out, int64_t(r) * H + c, y);
   }
   if (t < p.t_first) return;  // uniform per block
   const int orow = b * (p.bs - p.t_first) + (t - p.t_first);
   if (c < H) {
-    const float g = p.gain ? Act<T>::load(static_cast<const T*>(p.gain), c) : 1.0f;
-    Act<T>::store(static_cast<T*>(p.n_out), int64_t(orow) * H + c, y * g);
+    const V g = p.gain ? X::act(static_cast<const T*>(p.gain), c) : X::splat(1.f);
+    X::put(static_cast<T*>(p.n_out), int64_t(orow) * H + c, y * g);
   }
-  const float ss = block_sum(y * y, red);
-  if (threadIdx.x == 0) p.sumsq[int64_t(orow) * gridDim.y + blockIdx.y] = ss;
+  const int nslots = norm_col_blocks_dev(H);
+  if (VEC == 1) {
+    const float ss = block_sum(X::sq(y), red);
+    if (threadIdx.x == 0) p.sumsq[int64_t(orow) * nslots + blockIdx.y] = ss;
+  } else {
+    const float ss = wave_sum(X::sq(y));
+    const int slot = blockIdx.y * (256 * VEC / 256) + int(threadIdx.x) / WAVE;
+    if ((threadIdx.x & (WAVE - 1)) == 0 && slot < nslots) p.sumsq[int64_t(orow) * nslots + slot] = ss;
+  }
 }
 
 // Rotate-half RoPE angle for pair i of a head of width d at position pos,
@@ -206,12 +288,20 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluArgs p) {
   Act<T>::store(static_cast<T*>(p.out), idx, gt / (1.0f + expf(-gt)) * up);
 }
 
-int norm_col_blocks(int H) { return (H + 255) / 256; }
+int norm_col_blocks(int H) { return norm_col_blocks_dev(H); }
 
 void launch_norm(bool f32, const NormArgs& a, hipStream_t s) {
-  dim3 grid(a.rows, norm_col_blocks(a.H));
-  if (f32) hipLaunchKernelGGL(resconv_kernel<float>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(resconv_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  // few rows: one element per thread (more blocks, shorter chains); many
+  // rows: four per thread (16-byte accesses)
+  const bool wide = a.rows > 64;
+  const dim3 grid(a.rows, wide ? (a.H + 1023) / 1024 : norm_col_blocks(a.H));
+  if (f32) {
+    if (wide) hipLaunchKernelGGL((resconv_kernel<float, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((resconv_kernel<float, 1>), grid, dim3(256), 0, s, a);
+  } else {
+    if (wide) hipLaunchKernelGGL((resconv_kernel<bf16_t, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((resconv_kernel<bf16_t, 1>), grid, dim3(256), 0, s, a);
+  }
 }
 
 void launch_qkv_epilogue(bool f32, const QkvEpiArgs& a, hipStream_t s) {
