@@ -235,6 +235,57 @@ __global__ __launch_bounds__(64) void qkv_epilogue_kernel(QkvEpiArgs p) {
   }
 }
 
+// Wide variant of qkv_epilogue_kernel: four consecutive pairs per thread
+// (16-byte partial loads), half / 4 threads per head, 64 / (half / 4) heads
+// per block of 64; grid = (M rows, ceil(heads / heads per block)).
+template <typename T>
+__global__ __launch_bounds__(64) void qkv_epilogue4_kernel(QkvEpiArgs p) {
+  const int d = p.d, half = d / 2, tph = half / 4, hpb = 64 / tph;
+  const int m = blockIdx.x;
+  const int h = blockIdx.y * hpb + int(threadIdx.x) / tph;
+  const int i = (int(threadIdx.x) % tph) * 4;
+  if (h >= p.nq + 2 * p.nkv) return;
+  const int b = m / p.bs, t = m % p.bs;
+  const int pos = p.ctx_lens[b] + t;
+  const int64_t row = int64_t(m) * p.ldp + int64_t(h) * d;
+  T* q = static_cast<T*>(p.q_out);
+  T* kc = static_cast<T*>(p.k_layer);
+  T* vc = static_cast<T*>(p.v_layer);
+  f32x4 x0 = sum_parts4(p.parts, p.splits, p.split_stride, row + i);
+  f32x4 x1 = sum_parts4(p.parts, p.splits, p.split_stride, row + i + half);
+  if (h < p.nq + p.nkv) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float c, sn;
+      rope_cs(pos, i + e, d, p.theta, c, sn);
+      const float y0 = x0[e] * c - x1[e] * sn;
+      const float y1 = x1[e] * c + x0[e] * sn;
+      x0[e] = y0;
+      x1[e] = y1;
+    }
+  }
+  if (h < p.nq) {
+    const int64_t o = (int64_t(m) * p.nq + h) * d;
+    Act4<T>::store(q, o + i, x0);
+    Act4<T>::store(q, o + i + half, x1);
+  } else if (pos >= 0 && pos < p.Lmax) {
+    if (h < p.nq + p.nkv) {
+      const int g = h - p.nq;
+      const int64_t o = ((int64_t(b) * p.nkv + g) * p.Lmax + pos) * d;
+      Act4<T>::store(kc, o + i, x0);
+      Act4<T>::store(kc, o + i + half, x1);
+    } else {
+      const int g = h - p.nq - p.nkv;
+      const int64_t o = (int64_t(b) * p.nkv + g) * d * p.Lmax + pos;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Act<T>::store(vc, o + int64_t(i + e) * p.Lmax, x0[e]);
+        Act<T>::store(vc, o + int64_t(i + e + half) * p.Lmax, x1[e]);
+      }
+    }
+  }
+}
+
 // grid = (Mn rows, nL * 2 nkv), block = 64.  New context row r belongs to the
 // sequence b with offsets[b] <= r < offsets[b + 1] and sits at position
 // ctx_lens[b] - n_b + (r - offsets[b]).
@@ -276,16 +327,21 @@ __global__ __launch_bounds__(64) void kv_append_kernel(KvAppendArgs p) {
   }
 }
 
-// act[m][f] = SiLU(gate) * up, gate = row m col f, up = col F + f.
-template <typename T>
+// act[m][f] = SiLU(gate) * up, gate = row m col f, up = col F + f; VEC
+// consecutive f per thread (F is a multiple of 32).
+template <typename T, int VEC>
 __global__ __launch_bounds__(256) void swiglu_kernel(SwigluArgs p) {
-  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  typedef Vec<T, VEC> X;
+  const int64_t idx = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * VEC;
   if (idx >= int64_t(p.M) * p.F) return;
   const int m = int(idx / p.F), f = int(idx % p.F);
   const int64_t base = int64_t(m) * p.ldp;
-  const float gt = sum_parts(p.parts, p.splits, p.split_stride, base + f);
-  const float up = sum_parts(p.parts, p.splits, p.split_stride, base + p.F + f);
-  Act<T>::store(static_cast<T*>(p.out), idx, gt / (1.0f + expf(-gt)) * up);
+  const typename X::V gt = X::parts(p.parts, p.splits, p.split_stride, base + f);
+  const typename X::V up = X::parts(p.parts, p.splits, p.split_stride, base + p.F + f);
+  typename X::V y;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) y[e] = gt[e] / (1.0f + expf(-gt[e])) * up[e];
+  X::put(static_cast<T*>(p.out), idx, y);
 }
 
 int norm_col_blocks(int H) { return norm_col_blocks_dev(H); }
@@ -305,6 +361,14 @@ void launch_norm(bool f32, const NormArgs& a, hipStream_t s) {
 }
 
 void launch_qkv_epilogue(bool f32, const QkvEpiArgs& a, hipStream_t s) {
+  if (a.M > 64) {
+    // many rows: four pairs per thread, 16-byte partial loads
+    const int hpb = 64 / (a.d / 8);
+    const dim3 grid(a.M, (a.nq + 2 * a.nkv + hpb - 1) / hpb);
+    if (f32) hipLaunchKernelGGL(qkv_epilogue4_kernel<float>, grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(qkv_epilogue4_kernel<bf16_t>, grid, dim3(64), 0, s, a);
+    return;
+  }
   dim3 grid(a.M, a.nq + 2 * a.nkv);
   if (f32) hipLaunchKernelGGL(qkv_epilogue_kernel<float>, grid, dim3(64), 0, s, a);
   else hipLaunchKernelGGL(qkv_epilogue_kernel<bf16_t>, grid, dim3(64), 0, s, a);
@@ -318,9 +382,15 @@ void launch_kv_append(bool f32, const KvAppendArgs& a, hipStream_t s) {
 
 void launch_swiglu(bool f32, const SwigluArgs& a, hipStream_t s) {
   const int64_t n = int64_t(a.M) * a.F;
-  dim3 grid(unsigned((n + 255) / 256));
-  if (f32) hipLaunchKernelGGL(swiglu_kernel<float>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(swiglu_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  const bool wide = a.M > 64;
+  const dim3 grid(unsigned(wide ? (n / 4 + 255) / 256 : (n + 255) / 256));
+  if (f32) {
+    if (wide) hipLaunchKernelGGL((swiglu_kernel<float, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((swiglu_kernel<float, 1>), grid, dim3(256), 0, s, a);
+  } else {
+    if (wide) hipLaunchKernelGGL((swiglu_kernel<bf16_t, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((swiglu_kernel<bf16_t, 1>), grid, dim3(256), 0, s, a);
+  }
 }
 
 }  // namespace dfl
