@@ -239,7 +239,7 @@ const void* byte_offset(const void* p, int64_t bytes) {
   return static_cast<const char*>(p) + bytes;
 }
 
-constexpr size_t kSelectLds = 120 * 1024;  // one window covers every position at the configs here
+constexpr size_t kSelectLds = 156 * 1024;  // one window covers every position at the configs here
 
 }  // namespace
 
