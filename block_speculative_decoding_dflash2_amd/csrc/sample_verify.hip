@@ -14,12 +14,17 @@
 // distribution is p_v = e_v / S over the kept set {v : key_v >= theta}, with
 // e_v = exp((z_v - m) / T).  theta and S are found without sorting the
 // vocabulary:
-//   * top-k: the k-th largest value is a radix select over the order-
-//     preserving 32-bit key of each logit (11 + 11 + 10 bit digits, one
-//     histogram pass per digit, LDS histograms); as soon as every element at
-//     or above the current bin fits in an LDS list (<= 2048 entries) the
-//     remaining work is an exact sort of that list;
-//   * top-p: the same radix select on the kept mass instead of the count.
+//   * top-k, common case: the row's first ids estimate (from a histogram of
+//     their keys) a bin low enough that at least k elements lie at or above
+//     it; one pass takes the row maximum and collects every element at or
+//     above that bin into an LDS list, which is sorted exactly;
+//   * top-k, otherwise (too few or too many collected): the k-th largest
+//     value by a radix select over the order-preserving 32-bit key of each
+//     logit (11 + 11 + 10 bit digits, one histogram pass per digit, LDS
+//     histograms), switching to the sorted list as soon as every element at
+//     or above the current bin fits it (<= 2048 entries);
+//   * top-p: the same radix select on the kept mass instead of the count,
+//     or the sorted list when it holds the kept set.
 // Weights are accumulated as 64-bit fixed-point integers E_v =
 // round(e_v * 2^s), s = 52 - ceil(log2 V), so every sum (histogram bins,
 // prefixes, totals) is exact and independent of the order of the atomics:
@@ -27,7 +32,8 @@
 // deterministic, and every total is exact in a double.  The decisions
 // u_i * S < E_d and the inverse-CDF draw are taken on these integers.
 // A second kernel (one workgroup per sequence) walks the accept decisions and
-// draws the bonus token by an exact prefix scan over the stop row.
+// draws the bonus token: from the kept set the row pass handed over when it
+// is small, else by an exact prefix scan over the stop row.
 #include <cfloat>
 #include <cmath>
 
