@@ -263,3 +263,18 @@ def test_draft_dynamic_conv(name, group):
         check_step(g, res, range(w.batch))
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name,overhead", [("small_bf16", "0"), ("small_fp32", "0"), ("small_fp8", "65536")])
+def test_draft_stream_split_planner_extremes(name, overhead, monkeypatch):
+    """Weight-streaming GEMMs (at most 64 rows) under the split planner's
+    extremes: a zero per-block cost (as many K splits as allowed) and a huge
+    one (the fewest waves): same checks as the default."""
+    monkeypatch.setenv("DFLASH2_STREAM_BLOCK_OVERHEAD", overhead)
+    w = synth.get(name)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()

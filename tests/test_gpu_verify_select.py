@@ -100,3 +100,27 @@ def test_select_matches_oracle(name, lattice):
         assert np.array_equal(got["pair"].cpu().numpy().view(np.uint32), want["pair"].view(np.uint32))
     finally:
         m.close()
+
+
+def test_select_largest_selector():
+    """selector_top_k 64 and selector_rank 256 (the ABI's limits): one LDS
+    window of ~152 KB; bit-exact paths, scores and pair scores, and the
+    confidence stop."""
+    w = synth.get("tiny_fp32").replace(top_k=64, rank=256, batch=3, selector_active=True)
+    tl, tr = synth.make_selector_tables(w)
+    inp = synth.make_selector_inputs(w, tag=9)
+    want = O.select_path(inp["anchors"], inp["ids"], inp["vals"], tl, tr)
+    conf = O.path_confidence(inp["anchors"], inp["ids"], inp["vals"], want["path"], tl, tr)
+    m = _select_model(w, tl, tr)
+    try:
+        a, i, v = (torch.from_numpy(inp[k]).cuda() for k in ("anchors", "ids", "vals"))
+        got = m.select_path(a, i, v, debug_pair=True)
+        stop = m.select_path_stop(a, i, v, p_min=0.0, want_conf=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(got["path"].cpu().numpy(), want["path"])
+        assert np.array_equal(got["score"].cpu().numpy().view(np.uint32), want["score"].view(np.uint32))
+        assert np.array_equal(got["pair"].cpu().numpy().view(np.uint32), want["pair"].view(np.uint32))
+        assert np.array_equal(stop["drafts"].cpu().numpy(), want["drafts"])
+        np.testing.assert_allclose(stop["conf"].cpu().numpy(), conf, rtol=0, atol=2e-6)
+    finally:
+        m.close()
