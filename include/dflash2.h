@@ -158,11 +158,13 @@ typedef struct dflash2_handle dflash2_handle;
  * (before any device work, the same rule the NIM page states for draft heads
  * in "Bring Your Own DFlash2 Head"): block_size < 2, num_q_heads not a
  * multiple of num_kv_heads, odd or oversized head_dim, conv_kernel_size
- * outside 1..block_size, selector_top_k outside 1..min(64, vocab),
- * selector_rank outside 1..256, mask_token_id outside [0, vocab), an unknown
- * weight_dtype, a null weight, a missing fp8 scale, and (UNSUPPORTED) any
- * contraction length (hidden, ffn, nq*head_dim, num_taps*tap_width) that is
- * not a multiple of 32.  The handle keeps a host copy of the config and the
+ * outside 1..block_size, conv_group_size that is negative or does not
+ * divide hidden, selector_top_k outside 1..min(64, vocab), selector_rank
+ * outside 1..256, mask_token_id outside [0, vocab), an unknown weight_dtype,
+ * a null weight (the static conv taps when conv_group_size is 0, the dynamic
+ * ones otherwise), a missing fp8 scale, and (UNSUPPORTED) any contraction
+ * length (hidden, ffn, nq*head_dim, num_taps*tap_width) that is not a
+ * multiple of 32, hidden > 16384 or max_context not a multiple of 8.  The handle keeps a host copy of the config and the
  * pointer table only; it is immutable and may be shared across threads and
  * streams. */
 dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weights* weights,
