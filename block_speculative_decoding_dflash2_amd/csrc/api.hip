@@ -513,17 +513,21 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
     aa.part_o = reinterpret_cast<float*>(ws + P.off_attn_o);
     aa.part_ml = reinterpret_cast<float*>(ws + P.off_attn_ml);
     aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(d)));
+    aa.o = obuf;  // used only with one chunk: the kernel then writes the output itself
+    const bool one_chunk = P.attn.nchunks == 1;
     // keys/values of every sequence at the host-side bound max_context
     const int64_t kv_bytes = int64_t(batch) * nkv * c.max_context * d * 2 * ab;
-    traced(stream, DFLASH2_K_ATTENTION, kv_bytes + int64_t(P.M) * qd * ab,
+    traced(stream, DFLASH2_K_ATTENTION, kv_bytes + int64_t(P.M) * qd * ab * (one_chunk ? 2 : 1),
            4 * int64_t(P.M) * qd * c.max_context, [&] { launch_attention(f32, aa, stream); });
-    AttnCombineArgs ca{};
-    ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.ctx_lens = ctx_lens;
-    ca.B = batch; ca.bs = bs; ca.nq = nq; ca.nkv = nkv; ca.d = d; ca.Lmax = c.max_context;
-    ca.window = c.sliding_window; ca.chunk_keys = P.attn.chunk; ca.nchunks = P.attn.nchunks;
-    ca.o = obuf;
-    traced(stream, DFLASH2_K_ATTN_COMBINE, int64_t(P.M) * qd * ab, 0,
-           [&] { launch_attn_combine(f32, ca, stream); });
+    if (!one_chunk) {
+      AttnCombineArgs ca{};
+      ca.part_o = aa.part_o; ca.part_ml = aa.part_ml; ca.ctx_lens = ctx_lens;
+      ca.B = batch; ca.bs = bs; ca.nq = nq; ca.nkv = nkv; ca.d = d; ca.Lmax = c.max_context;
+      ca.window = c.sliding_window; ca.chunk_keys = P.attn.chunk; ca.nchunks = P.attn.nchunks;
+      ca.o = obuf;
+      traced(stream, DFLASH2_K_ATTN_COMBINE, int64_t(P.M) * qd * ab, 0,
+             [&] { launch_attn_combine(f32, ca, stream); });
+    }
 
     gemm(obuf, qd, L.wo, fp8 ? L.wo_scale : nullptr, P.M, nullptr, H, qd, P.o, parts, plain);
     conv_norm(nullptr, h0, parts, &P.o, int64_t(P.M) * H, L.conv_ffn, L.dconv_ffn,

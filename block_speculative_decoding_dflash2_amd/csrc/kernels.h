@@ -126,6 +126,7 @@ struct AttnArgs {
   float* part_o;                  // [B][nkv][nchunks][QS][d]
   float* part_ml;                 // [B][nkv][nchunks][QS][2]
   float scale_log2;
+  void* o;                        // [B*bs][nq*d] act, written directly when nchunks == 1
 };
 
 struct AttnCombineArgs {
