@@ -24,22 +24,19 @@ namespace dfl {
 // This file is compiled with -ffp-contract=off: every product below is
 // rounded before it is added, and each pair's sum runs over m in order.
 // Rows are padded to RS = r rounded up to 4 floats (+4) so they can be read
-// 16 bytes at a time from LDS; four pairs are accumulated side by side.
-__device__ __forceinline__ void pair_dot4(const float* __restrict__ a0, const float* __restrict__ a1,
-                                          const float* __restrict__ a2, const float* __restrict__ a3,
-                                          const float* __restrict__ b0, const float* __restrict__ b1,
-                                          const float* __restrict__ b2, const float* __restrict__ b3,
-                                          int r, float (&out)[4]) {
+// 16 bytes at a time from LDS.
+// Pairs (a0, b0), (a0, b1), (a1, b0), (a1, b1), accumulated side by side.
+__device__ __forceinline__ void pair_dot2x2(const float* __restrict__ a0, const float* __restrict__ a1,
+                                            const float* __restrict__ b0, const float* __restrict__ b1, int r,
+                                            float (&out)[4]) {
   float c0 = 0.0f, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
   int m = 0;
   for (; m + 4 <= r; m += 4) {
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(a0 + m), y0 = *reinterpret_cast<const f32x4*>(b0 + m);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(a1 + m), y1 = *reinterpret_cast<const f32x4*>(b1 + m);
-    const f32x4 x2 = *reinterpret_cast<const f32x4*>(a2 + m), y2 = *reinterpret_cast<const f32x4*>(b2 + m);
-    const f32x4 x3 = *reinterpret_cast<const f32x4*>(a3 + m), y3 = *reinterpret_cast<const f32x4*>(b3 + m);
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(a0 + m), x1 = *reinterpret_cast<const f32x4*>(a1 + m);
+    const f32x4 y0 = *reinterpret_cast<const f32x4*>(b0 + m), y1 = *reinterpret_cast<const f32x4*>(b1 + m);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p0 = x0[e] * y0[e], p1 = x1[e] * y1[e], p2 = x2[e] * y2[e], p3 = x3[e] * y3[e];
+      const float p0 = x0[e] * y0[e], p1 = x0[e] * y1[e], p2 = x1[e] * y0[e], p3 = x1[e] * y1[e];
       c0 = c0 + p0;
       c1 = c1 + p1;
       c2 = c2 + p2;
@@ -47,7 +44,7 @@ __device__ __forceinline__ void pair_dot4(const float* __restrict__ a0, const fl
     }
   }
   for (; m < r; ++m) {
-    const float p0 = a0[m] * b0[m], p1 = a1[m] * b1[m], p2 = a2[m] * b2[m], p3 = a3[m] * b3[m];
+    const float p0 = a0[m] * b0[m], p1 = a0[m] * b1[m], p2 = a1[m] * b0[m], p3 = a1[m] * b1[m];
     c0 = c0 + p0;
     c1 = c1 + p1;
     c2 = c2 + p2;
@@ -58,15 +55,17 @@ __device__ __forceinline__ void pair_dot4(const float* __restrict__ a0, const fl
 
 __host__ __device__ int select_row_stride(int r) { return (r + 3) / 4 * 4 + 4; }
 
-// One block of 256 threads per sequence.  Pair scores depend only on the
-// candidate ids, so a window of `tw` transitions is done at once: the table
-// rows of its candidates are staged in LDS, all its pair scores are computed
-// in parallel, then wave 0 runs the max-sum recursion over the window (lane
-// j = candidate j; lanes of one wave run in lockstep, so S is read for every
-// i before any lane overwrites it).
+// One block of kSelThreads (1024) threads per sequence.  Pair scores depend
+// only on the candidate ids, so a window of `tw` transitions is done at once:
+// the table rows of its candidates are staged in LDS, all its pair scores are
+// computed in parallel, then wave 0 runs the max-sum recursion over the
+// window (lane j = candidate j, the scores S kept in registers; S in LDS
+// carries them from one window to the next).
 // LDS: TL [tw*k][RS], TR [tw*k][RS], PAIR [tw][k][k], S [k], BACK [P][k],
 // PATH [P], TOK [2*tw*k], VAL [tw*k], CONF [P].
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
+constexpr int kSelThreads = 1024;  // 16 waves: table gathers and pair scores in parallel
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs p, int tw) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -93,7 +92,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
     // current position's), then their table rows, all loads of a thread
     // issued before any is used
     const int nrows = 2 * nt * k;
-    for (int q = tid; q < nrows; q += 256) {
+    for (int q = tid; q < nrows; q += kSelThreads) {
       const bool right = q >= nt * k;
       const int rr = right ? q - nt * k : q;
       const int w = rr / k, i = rr - w * k, t = t0 + w;
@@ -102,15 +101,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
       else tok = t == 0 ? (i == 0 ? anchor : -1) : ids[(t - 1) * k + i];
       TOK[q] = (tok >= 0 && tok < V) ? tok : -1;
     }
-    for (int q = tid; q < nt * k; q += 256) VAL[q] = vals[t0 * k + q];
+    for (int q = tid; q < nt * k; q += kSelThreads) VAL[q] = vals[t0 * k + q];
     __syncthreads();
     if (vec4) {
       const int nv = r >> 2, total = nrows * nv;
-      for (int e0 = 0; e0 < total; e0 += 16 * 256) {
+      for (int e0 = 0; e0 < total; e0 += 16 * kSelThreads) {
         f32x4 v[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          const int e = e0 + u * 256 + tid;
+          const int e = e0 + u * kSelThreads + tid;
           const int row = e / nv, mv = e - row * nv;
           const int tok = e < total ? TOK[row] : -1;
           const float* table = row >= nt * k ? p.tr : p.tl;
@@ -119,7 +118,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          const int e = e0 + u * 256 + tid;
+          const int e = e0 + u * kSelThreads + tid;
           const int row = e / nv, mv = e - row * nv;
           if (e < total) {
             float* dst = row >= nt * k ? TR + (row - nt * k) * rs : TL + row * rs;
@@ -129,11 +128,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
       }
     } else {
       const int total = nrows * r;
-      for (int e0 = 0; e0 < total; e0 += 8 * 256) {
+      for (int e0 = 0; e0 < total; e0 += 8 * kSelThreads) {
         float v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * 256 + tid;
+          const int e = e0 + u * kSelThreads + tid;
           const int row = e / r, m = e - row * r;
           const int tok = e < total ? TOK[row] : -1;
           const float* table = row >= nt * k ? p.tr : p.tl;
@@ -141,7 +140,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * 256 + tid;
+          const int e = e0 + u * kSelThreads + tid;
           const int row = e / r, m = e - row * r;
           if (e < total) {
             float* dst = row >= nt * k ? TR + (row - nt * k) * rs : TL + row * rs;
@@ -151,73 +150,70 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
       }
     }
     __syncthreads();
-    // ---- pair scores of the window: PAIR[w][i][j] = pi(prev_i, cur_j)
-    const int npairs = nt * k * k;
-    for (int q0 = tid; q0 < npairs; q0 += 4 * 256) {
-      int qi[4];
-      const float* ap[4];
-      const float* bp[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        qi[u] = q0 + u * 256;
-        const int qq = qi[u] < npairs ? qi[u] : q0;
-        const int w = qq / (k * k), ij = qq - w * k * k, i = ij / k, j = ij - i * k;
-        ap[u] = TL + (w * k + i) * rs;
-        bp[u] = TR + (w * k + j) * rs;
-      }
+    // ---- pair scores of the window: PAIR[w][i][j] = pi(prev_i, cur_j).  A
+    // thread takes a 2 x 2 block (rows i0, i0 + 1 against columns j0, j0 + 1)
+    // so each staged row read from LDS feeds two chains.
+    const int kh = (k + 1) >> 1;
+    const int nblk = nt * kh * kh;
+    for (int q = tid; q < nblk; q += kSelThreads) {
+      const int w = q / (kh * kh), ij = q - w * kh * kh;
+      const int i0 = 2 * (ij / kh), j0 = 2 * (ij - (ij / kh) * kh);
+      const int i1 = min(i0 + 1, k - 1), j1 = min(j0 + 1, k - 1);
+      const float* a0 = TL + (w * k + i0) * rs;
+      const float* a1 = TL + (w * k + i1) * rs;
+      const float* b0 = TR + (w * k + j0) * rs;
+      const float* b1 = TR + (w * k + j1) * rs;
       float out[4];
-      pair_dot4(ap[0], ap[1], ap[2], ap[3], bp[0], bp[1], bp[2], bp[3], r, out);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (qi[u] < npairs) PAIR[qi[u]] = out[u];
+      pair_dot2x2(a0, a1, b0, b1, r, out);
+      float* dst = PAIR + w * k * k;
+      dst[i0 * k + j0] = out[0];
+      if (j0 + 1 < k) dst[i0 * k + j0 + 1] = out[1];
+      if (i0 + 1 < k) dst[(i0 + 1) * k + j0] = out[2];
+      if (i0 + 1 < k && j0 + 1 < k) dst[(i0 + 1) * k + j0 + 1] = out[3];
     }
     __syncthreads();
     if (p.debug_pair) {
-      for (int q = tid; q < npairs; q += 256) {
+      const int npairs = nt * k * k;
+      for (int q = tid; q < npairs; q += kSelThreads) {
         const int w = q / (k * k), ij = q - w * k * k, i = ij / k, j = ij - i * k;
         const int t = t0 + w;
         p.debug_pair[(int64_t(b) * P + t) * k * k + ij] = PAIR[w * k * k + (t == 0 ? 0 : i) * k + j];
       }
     }
-    // ---- max-sum recursion over the window (wave 0)
+    // ---- max-sum recursion over the window (wave 0, lane j = candidate j).
+    // The previous scores stay in registers and are broadcast with readlane;
+    // every lane runs the same loads (lanes past k read candidate k - 1 and
+    // store nothing), so the loop has no divergent branches.
     if (tid < WAVE) {
+      const int j = tid, jj = min(j, k - 1);
+      float s_cur = S[jj];
       for (int w = 0; w < nt; ++w) {
         const int t = t0 + w;
         const float* pr = PAIR + w * k * k;
-        float snew = 0.f;
+        float snew;
         int bi = 0;
-        if (tid < k) {
-          const int j = tid;
-          if (t == 0) {
-            snew = pr[j] + VAL[j];
-          } else {
-            float bv = 0.f;
-            for (int i0 = 0; i0 < k; i0 += 8) {
-              float sv[8], pv[8];
+        if (t == 0) {
+          snew = pr[jj] + VAL[jj];
+        } else {
+          float bv = 0.f;
+          for (int i0 = 0; i0 < k; i0 += 16) {  // 16 column entries per LDS round trip
+            float pv[16];
 #pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u;
-                sv[u] = i < k ? S[i] : 0.f;
-                pv[u] = i < k ? pr[i * k + j] : 0.f;
-              }
+            for (int u = 0; u < 16; ++u) pv[u] = pr[min(i0 + u, k - 1) * k + jj];
 #pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u;
-                const float v = sv[u] + pv[u];
-                if (i == 0) bv = v;
-                else if (i < k && v > bv) { bv = v; bi = i; }
-              }
+            for (int u = 0; u < 16; ++u) {
+              const int i = i0 + u;
+              const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_cur), min(i, k - 1))) + pv[u];
+              if (i == 0) bv = v;
+              else if ((i < k) & (v > bv)) { bv = v; bi = i; }
             }
-            snew = bv + VAL[w * k + j];
           }
+          snew = bv + VAL[w * k + jj];
         }
-        __builtin_amdgcn_wave_barrier();
-        if (tid < k) {
-          S[tid] = snew;
-          BACK[t * k + tid] = bi;
-        }
-        __builtin_amdgcn_wave_barrier();
+        s_cur = snew;
+        if (j < k) BACK[t * k + j] = bi;
       }
+      if (j < k) S[j] = s_cur;
     }
     __syncthreads();
   }
@@ -234,7 +230,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
     }
   }
   __syncthreads();
-  for (int t = tid; t < P; t += 256) {
+  for (int t = tid; t < P; t += kSelThreads) {
     const int j = PATH[t];
     p.path[int64_t(b) * P + t] = j;
     p.drafts[int64_t(b) * P + t] = ids[t * k + j];
@@ -248,7 +244,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs p, int tw) {
   // pi is summed in the selector's order (multiply, then add, m ascending).
   float* CONF = VAL + tw * k;  // [P]
   const int wave = tid / WAVE, lane = tid & (WAVE - 1);
-  for (int t = wave; t < P; t += 256 / WAVE) {
+  for (int t = wave; t < P; t += kSelThreads / WAVE) {
     const int prev = t == 0 ? anchor : ids[(t - 1) * k + PATH[t - 1]];
     float sj = -INFINITY;
     if (lane < k) {
@@ -317,7 +313,7 @@ static size_t select_lds_bytes(int k, int r, int P, int tw) {
 }
 
 void launch_select(const SelectArgs& a, int tw, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(256), select_lds_bytes(a.k, a.r, a.P, tw), s, a, tw);
+  hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(kSelThreads), select_lds_bytes(a.k, a.r, a.P, tw), s, a, tw);
 }
 
 // grid = (nchunks, B * bs), block = 256: best (value, id) key of one chunk.
