@@ -71,7 +71,11 @@ template <> struct WLds<bf16_t> {
   typedef u32x4 raw;
 };
 template <> struct WLds<fp8_t> {
-  static constexpr int ROWB = 80;
+  // 72-byte rows: the 8-byte operand reads of 32 consecutive rows then fall
+  // on distinct banks (an 80-byte pitch maps rows r and r + 16 onto the same
+  // banks; measured bank-conflict cycles were as many as the LDS busy cycles).
+  // Rows are no longer 16-byte aligned, so they are written 8 bytes at a time.
+  static constexpr int ROWB = 72;
   static constexpr int NLD = 4;      // 16 rows x 64 B each
   typedef u32x4 raw;
 };
@@ -135,7 +139,15 @@ struct TiledMain {
     };
     auto store_w = [&]() {
 #pragma unroll
-      for (int q = 0; q < NLD; ++q) *reinterpret_cast<u32x4*>(wdst + q * RPI * WROWB) = wr[q];
+      for (int q = 0; q < NLD; ++q) {
+        char* d = wdst + q * RPI * WROWB;
+        if constexpr (WROWB % 16 == 0) {
+          *reinterpret_cast<u32x4*>(d) = wr[q];
+        } else {
+          *reinterpret_cast<u32x2*>(d) = u32x2{wr[q][0], wr[q][1]};
+          *reinterpret_cast<u32x2*>(d + 8) = u32x2{wr[q][2], wr[q][3]};
+        }
+      }
     };
     auto load_x = [&](int kt) {
 #pragma unroll
