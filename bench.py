@@ -227,8 +227,18 @@ def main():
                 f"{dd['bytes'] / max(dd['ms'], 1e-9) / 1e6:8.1f} GB/s")
         log(f"  kernel time {traced_total * 1e3 / args.steps:.1f} us/step (wall {s_step * 1e6:.1f})")
 
-    acc = accepted.cpu().numpy()
-    spec = speculative_metrics(acc.tolist(), bs - 1)
+    # acceptance of the planted verifier: the timed steps verify one planted
+    # draw per sequence; with few sequences that is too few samples, so more
+    # independent planted draws (untimed) are verified until at least 64
+    # sequence-steps are counted
+    acc = accepted.cpu().numpy().tolist()
+    if sampling is None:
+        for tag in range(1, -(-64 // B)):
+            t_extra = torch.from_numpy(synth.make_target_logits(w, drafts.cpu().numpy(), tag=tag)).to(dev)
+            verify_accept(drafts, t_extra, workspace=vws, accepted=accepted, bonus=bonus)
+            acc += accepted.cpu().numpy().tolist()
+            del t_extra
+    spec = speculative_metrics(acc, bs - 1)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -274,7 +284,8 @@ def main():
         "draft_tokens_per_s": round(B * (bs - 1) / s_step, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "acceptance": {kk: spec[kk] for kk in ("draft_acceptance_rate", "mean_acceptance_length")},
+        "acceptance": dict({kk: spec[kk] for kk in ("draft_acceptance_rate", "mean_acceptance_length")},
+                           sequence_steps=spec["num_spec_steps"]),
         "kernels_us_per_step": {kk: round(dd["ms"] * 1e3 / args.steps, 2) for kk, dd in per_kind.items()},
     }
     print(json.dumps(out), flush=True)
