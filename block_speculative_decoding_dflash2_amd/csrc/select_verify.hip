@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs p, int t
     // store nothing), so the loop has no divergent branches.
     if (tid < WAVE) {
       const int j = tid, jj = min(j, k - 1);
-      float s_cur = S[jj];
+      float s_cur = t0 > 0 ? S[jj] : 0.f;  // scores carried from the previous window
       for (int w = 0; w < nt; ++w) {
         const int t = t0 + w;
         const float* pr = PAIR + w * k * k;
