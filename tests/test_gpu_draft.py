@@ -237,10 +237,13 @@ def test_draft_tiled_single_split(name, monkeypatch):
         g.close()
 
 
-@pytest.mark.parametrize("name,window", [("small_bf16", 64), ("medium_fp8", 100), ("small_fp32", 33)])
+@pytest.mark.parametrize("name,window", [("small_bf16", 64), ("medium_fp8", 100), ("small_fp32", 33),
+                                         ("tiny_fp32", 8)])
 def test_draft_sliding_window(name, window):
     """draft_sliding_window: attention reaches back `window` context rows;
-    sequences both shorter and longer than the window."""
+    sequences both shorter and longer than the window.  tiny_fp32 plans one
+    key chunk, so the attention kernel writes its output without the merge
+    pass; the others merge several chunks."""
     w = synth.get(name).replace(sliding_window=window)
     g = DraftRun(w)
     try:
