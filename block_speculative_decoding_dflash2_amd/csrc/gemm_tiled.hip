@@ -159,6 +159,7 @@ struct TiledMain {
         *reinterpret_cast<u32x4*>(xdst + buf * XBUF + q * 32 * kTXRow) = xs[q];
     };
     auto compute = [&](int buf) {
+      __builtin_amdgcn_s_setprio(1);  // the wave with matrix work ready issues first
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         Frag8Bf16 wf[2];
@@ -176,6 +177,7 @@ struct TiledMain {
           for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i].v, xf, acc[i][j], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // W(kt) sits in registers at the start of stage kt and is copied to this
     // wave's LDS region; X(kt) is in LDS buffer kt & 1.
