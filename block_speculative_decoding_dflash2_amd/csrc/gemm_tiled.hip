@@ -494,8 +494,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int BM = Main::BM, F2 = Main::F2;
   constexpr int XB = Main::LDS_BYTES;
   constexpr int CB = BM * kTSlots * 8;   // candidate slots
+  constexpr int SB = 4 * WAVE * 36 * 4;  // per-wave staging of one row's 32 values per lane (append)
   constexpr int TB = 64 * 260 * 4;       // 64 rows of tile values (overflow path)
-  constexpr int LB = XB > CB ? (XB > TB ? XB : TB) : (CB > TB ? CB : TB);
+  constexpr int CSB = CB + SB;
+  constexpr int LB = XB > CSB ? (XB > TB ? XB : TB) : (CSB > TB ? CSB : TB);
   __shared__ __attribute__((aligned(16))) char lds[LB];
   __shared__ float inv[BM];
   __shared__ float thr[BM];       // first tile: float bound T
@@ -597,6 +599,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // append the lane's passing values of each of its rows: one atomic per
     // row for the lane's count, then the keys at consecutive slots
+    // append the lane's passing values of each of its rows: one atomic per
+    // row for the lane's count, then the keys at consecutive slots.  The
+    // lane's 32 values of a row are staged in its own LDS row so that only
+    // the set bits of its mask are visited (a short divergent loop) instead
+    // of testing all 32 values with a branch each.
+    float* stage = reinterpret_cast<float*>(lds + CB) + (wave * WAVE + lane) * 36;
     auto append = [&](const uint32_t (&mask)[F2]) {
       int base[F2];
 #pragma unroll
@@ -606,18 +614,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
 #pragma unroll
       for (int j = 0; j < F2; ++j) {
-        int pos = base[j];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if ((mask[j] >> (16 * i + v)) & 1u) {
-              if (pos < kTSlots) {
-                slots[(32 * j + r) * kTSlots + pos] =
-                    rank_key(acc[i][j][v], uint32_t(n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3)));
-              }
-              ++pos;
-            }
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(stage + 16 * i + 4 * q) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        uint32_t m = mask[j];
+        int pos = base[j];
+        uint64_t* dst = slots + (32 * j + r) * kTSlots;
+        while (m != 0u && pos < kTSlots) {
+          const int bit = __builtin_ctz(m);
+          m &= m - 1u;
+          const int v = bit & 15;
+          const uint32_t id = uint32_t(n0w + 32 * (bit >> 4) + 8 * (v >> 2) + 4 * h + (v & 3));
+          dst[pos] = rank_key(stage[bit], id);
+          ++pos;
+        }
       }
     };
     {
