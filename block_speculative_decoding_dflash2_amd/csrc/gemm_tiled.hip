@@ -598,13 +598,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();  // ab is dead from here; its space holds the candidate slots
 
     // append the lane's passing values of each of its rows: one atomic per
-    // row for the lane's count, then the keys at consecutive slots
-    // append the lane's passing values of each of its rows: one atomic per
     // row for the lane's count, then the keys at consecutive slots.  The
     // lane's 32 values of a row are staged in its own LDS row so that only
     // the set bits of its mask are visited (a short divergent loop) instead
     // of testing all 32 values with a branch each.
-    float* stage = reinterpret_cast<float*>(lds + CB) + (wave * WAVE + lane) * 36;
+    float* vstage = reinterpret_cast<float*>(lds + CB) + (wave * WAVE + lane) * 36;
     auto append = [&](const uint32_t (&mask)[F2]) {
       int base[F2];
 #pragma unroll
@@ -618,7 +616,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<f32x4*>(stage + 16 * i + 4 * q) =
+            *reinterpret_cast<f32x4*>(vstage + 16 * i + 4 * q) =
                 f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         uint32_t m = mask[j];
         int pos = base[j];
@@ -628,7 +626,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           m &= m - 1u;
           const int v = bit & 15;
           const uint32_t id = uint32_t(n0w + 32 * (bit >> 4) + 8 * (v >> 2) + 4 * h + (v & 3));
-          dst[pos] = rank_key(stage[bit], id);
+          dst[pos] = rank_key(vstage[bit], id);
           ++pos;
         }
       }
