@@ -2,9 +2,9 @@
 //
 // Selector (NeMo AutoModel page, "Variants": a pairwise path selector walks
 // one coherent path through each position's top-k candidates; "Objective":
-// candidates are scored against the predecessor): one wavefront per
-// sequence.  Per transition the factor-table rows of the previous and the
-// current candidates are staged in LDS, all k*k pair scores are computed in
+// candidates are scored against the predecessor): one block per sequence.
+// Per transition the factor-table rows of the previous and the current
+// candidates are staged in LDS, all k*k pair scores are computed in
 // float32 with separate multiply and add (m ascending), and a max-sum
 // (Viterbi) step keeps the smallest predecessor on ties; the path is then
 // traced back.  Only the listed order of float32 operations is used, so the
