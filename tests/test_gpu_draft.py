@@ -281,3 +281,27 @@ def test_draft_stream_split_planner_extremes(name, overhead, monkeypatch):
         check_step(g, res, range(w.batch))
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name,tag,changes", [
+    ("tiny_fp32", "bs2", dict(block_size=2)),          # one draft position: the lattice is one transition
+    ("small_bf16", "bs2", dict(block_size=2)),
+    ("small_bf16", "k1", dict(top_k=1)),               # one candidate per position: the path is forced
+    ("medium_fp8", "k1", dict(top_k=1)),               # ... on the tiled lm_head
+    ("small_fp32", "ctx1", dict(cold=True, ctx=(1, 3))),  # contexts of 1-3 rows, all appended this step
+    ("small_bf16", "ctx1", dict(cold=True, ctx=(1, 3))),
+])
+def test_draft_degenerate_shapes(name, tag, changes):
+    """The method's degenerate cases: block size 2, top-k 1 and contexts of
+    one to three rows (a 32-row cache shorter than one key sub-chunk).  Same
+    checks as the default workloads."""
+    w = synth.get(name).replace(name=f"{name}_{tag}", **changes)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        if w.top_k == 1:  # the path is forced on both sides: drafts are the top-1 ids
+            assert (res["path"] == 0).all()
+            assert (g.path == 0).all() and np.array_equal(g.drafts, g.topk_ids[..., 0])
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()

@@ -124,3 +124,31 @@ def test_select_largest_selector():
         np.testing.assert_allclose(stop["conf"].cpu().numpy(), conf, rtol=0, atol=2e-6)
     finally:
         m.close()
+
+
+@pytest.mark.parametrize("k,bs,r", [(1, 8, 8), (3, 8, 8), (5, 2, 6), (33, 6, 12), (17, 16, 5)])
+def test_select_odd_and_degenerate(k, bs, r):
+    """Odd candidate counts (the last row and column of the 2 x 2 pair
+    blocks are half used), k past a multiple of 16 (a ragged last round of
+    the recursion's column reads), k = 1, one draft position, and ranks that
+    are not a multiple of 4 (scalar table staging): bit-exact paths, scores,
+    pair scores and confidences."""
+    w = synth.get("tiny_fp32").replace(top_k=k, block_size=bs, rank=r, batch=4, selector_active=True)
+    tl, tr = synth.make_selector_tables(w)
+    inp = synth.make_selector_inputs(w, tag=11)
+    want = O.select_path(inp["anchors"], inp["ids"], inp["vals"], tl, tr)
+    conf = O.path_confidence(inp["anchors"], inp["ids"], inp["vals"], want["path"], tl, tr)
+    m = _select_model(w, tl, tr)
+    try:
+        a, i, v = (torch.from_numpy(inp[key]).cuda() for key in ("anchors", "ids", "vals"))
+        got = m.select_path(a, i, v, debug_pair=True)
+        stop = m.select_path_stop(a, i, v, p_min=0.0, want_conf=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(got["path"].cpu().numpy(), want["path"])
+        assert np.array_equal(got["drafts"].cpu().numpy(), want["drafts"])
+        assert np.array_equal(got["score"].cpu().numpy().view(np.uint32), want["score"].view(np.uint32))
+        assert np.array_equal(got["pair"].cpu().numpy().view(np.uint32), want["pair"].view(np.uint32))
+        assert np.array_equal(stop["drafts"].cpu().numpy(), want["drafts"])
+        np.testing.assert_allclose(stop["conf"].cpu().numpy(), conf, rtol=0, atol=2e-6)
+    finally:
+        m.close()
