@@ -306,13 +306,21 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkMergeArgs p) {
   uint64_t best[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) best[j] = 0ull;
-  for (int gi = tid; gi < groups; gi += NT) {
-    uint64_t brev[KMAX];
+  // each thread's next list is loaded while the current one is merged
+  auto load_rev = [&](uint64_t (&dst)[KMAX], int gi) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const int src = KMAX - 1 - j;                 // reversed: ascending
-      brev[j] = src < p.glen ? c[int64_t(gi) * p.glen + src] : 0ull;
+      dst[j] = (gi < groups && src < p.glen) ? c[int64_t(gi) * p.glen + src] : 0ull;
     }
+  };
+  uint64_t nxt[KMAX];
+  load_rev(nxt, tid);
+  for (int gi = tid; gi < groups; gi += NT) {
+    uint64_t brev[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) brev[j] = nxt[j];
+    load_rev(nxt, gi + NT);
     bitonic_top<KMAX>(best, brev);
   }
   for (int d = 1; d < WAVE; d <<= 1) {

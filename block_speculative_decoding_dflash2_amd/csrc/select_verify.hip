@@ -327,7 +327,21 @@ __global__ __launch_bounds__(256) void verify_partial_kernel(VerifyArgs p) {
   if ((p.V & 3) == 0) {
     const int a0 = v0 >> 2, a1 = v1 >> 2;  // chunk is a multiple of 4
     const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
-    for (int i = a0 + threadIdx.x; i < a1; i += blockDim.x) {
+    const int nt = blockDim.x;
+    int i = a0 + threadIdx.x;
+    for (; i + 3 * nt < a1; i += 4 * nt) {  // four loads in flight per thread
+      f32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = z4[i + u * nt];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint64_t kk = rank_key(x[u][e], uint32_t(4 * (i + u * nt) + e));
+          best = kk > best ? kk : best;
+        }
+    }
+    for (; i < a1; i += nt) {
       const f32x4 x = z4[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
