@@ -121,6 +121,10 @@ def test_logit_transform():
     assert np.all(np.abs(y) < 10.0) and np.allclose(y, -O.logit_transform(-x, 0.5, 10.0))
     assert np.all(np.diff(y) > 0)
     assert np.isclose(O.logit_transform(np.array([1e-4]), 0.5, 10.0)[0], 0.5e-4, rtol=1e-8)
+    # multiplier first, then the cap: 0.5 * 20 = 10 -> 10 tanh(1); large inputs
+    # saturate at the cap itself, not at multiplier * cap
+    assert np.isclose(O.logit_transform(np.array([20.0]), 0.5, 10.0)[0], 10.0 * math.tanh(1.0), rtol=1e-14)
+    assert np.isclose(O.logit_transform(np.array([1e4]), 0.5, 10.0)[0], 10.0, rtol=1e-14)
 
 
 # ------------------------------------------------- dynamic convolution
