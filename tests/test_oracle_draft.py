@@ -42,7 +42,7 @@ def test_zero_sublayer_outputs_leave_conv_chain():
     """With W_o = 0 and W_down = 0 attention and FFN add nothing, so the
     residual stream is the embedding pushed through the 2 * nL block
     convolutions, and the logits are RMSNorm of rows 1.. times lm_head."""
-    w = W0.replace(num_layers=2)
+    w = W0.replace(num_layers=2, input_embedding_scale=2.5)
     W, inp = _setup(w)
     for layer in W.layers:
         layer.wo = encode(np.zeros(layer.wo.shape, np.float32), "fp32")
@@ -60,6 +60,56 @@ def test_zero_sublayer_outputs_leave_conv_chain():
         r = h[1:]
         n = r / np.sqrt((r ** 2).mean(axis=1, keepdims=True) + w.rms_eps) * g
         assert np.allclose(out["zeta"][b], n @ W.lm_head.data.astype(np.float64).T, rtol=1e-10, atol=1e-13)
+
+
+def test_swiglu_gate_half_takes_the_silu():
+    """With W_o = 0 and an FFN whose gate row 0 reads 2 n_0, up row 0 reads
+    n_0 and W_down writes act_0 back to channel 0 (all else zero), the layer
+    adds SiLU(2 n_0) * n_0 to channel 0 and nothing elsewhere (SwiGLU: the
+    SiLU acts on the gate half of W_gate_up, the first ffn rows)."""
+    w = W0.replace(num_layers=1)
+    W, inp = _setup(w)
+    layer = W.layers[0]
+    H, F = w.hidden, w.ffn
+    layer.wo = encode(np.zeros(layer.wo.shape, np.float32), "fp32")
+    gu = np.zeros((2 * F, H), np.float32)
+    gu[0, 0], gu[F, 0] = 2.0, 1.0
+    layer.w_gate_up = encode(gu, "fp32")
+    down = np.zeros((H, F), np.float32)
+    down[0, 0] = 1.0
+    layer.w_down = encode(down, "fp32")
+    out, _, _ = _run(w, W, inp)
+    E = W.embed.data.astype(np.float64)
+    for b in range(len(inp.anchors)):
+        toks = [int(inp.anchors[b])] + [w.mask_token_id] * (w.block_size - 1)
+        h = _conv2(_conv2(w.input_embedding_scale * E[toks], layer.conv_attn.data.astype(np.float64)),
+                   layer.conv_ffn.data.astype(np.float64))
+        g = layer.ffn_norm.data.astype(np.float64)
+        n0 = (h / np.sqrt((h ** 2).mean(axis=1, keepdims=True) + w.rms_eps) * g)[:, 0]
+        want = h.copy()
+        want[:, 0] += (2 * n0) / (1 + np.exp(-2 * n0)) * n0
+        assert np.allclose(out["h_final"][b], want, rtol=1e-12, atol=1e-14)
+
+
+def test_only_relative_positions_matter():
+    """RoPE makes every attention score depend on position differences only.
+    Moving the context and the block 29 positions later (29 other rows are
+    appended first and a sliding window of exactly the 12 real rows hides
+    them) must leave the logits unchanged up to the float32 rounding of the
+    stored keys."""
+    L, delta = 12, 29
+    w = TINY_FP32.replace(batch=1, ctx=(L, L), cold=True, sliding_window=L, spare_context=40)
+    W, inp = _setup(w)
+    assert w.max_context >= delta + L + w.block_size
+    kc, vc = O.new_cache(w, 1)
+    O.append_context(w, W, kc, vc, inp.taps, inp.new_offsets, inp.ctx_lens)
+    a = O.draft_block(w, W, kc, vc, inp.anchors, inp.ctx_lens)["zeta"]
+    kc2, vc2 = O.new_cache(w, 1)
+    other = np.random.default_rng(21).standard_normal((delta, w.num_taps, w.tap_width)).astype(np.float32)
+    O.append_context(w, W, kc2, vc2, encode(other, "fp32"), np.array([0, delta]), np.array([delta]))
+    O.append_context(w, W, kc2, vc2, inp.taps, np.array([0, L]), np.array([delta + L]))
+    b = O.draft_block(w, W, kc2, vc2, inp.anchors, np.array([delta + L]))["zeta"]
+    assert np.allclose(a, b, rtol=0, atol=1e-6 * np.abs(a).max())
 
 
 def test_uniform_attention_averages_all_values():

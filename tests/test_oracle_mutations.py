@@ -203,3 +203,70 @@ def test_pins_pass_on_the_oracle_itself():
     for pins in (OPS, DRAFT, SELECT, TOPK, VERIFY):
         for pin in pins:
             pin()
+
+
+# ------------------------------------------------------------------ composed forward
+# Mistakes inside append_context / draft_block are planted in a copy of the
+# oracle's source (one exact text replacement each), executed as a separate
+# module; the invariant pins of the composed forward must notice.
+
+import inspect
+import types
+
+_SRC = inspect.getsource(OD)
+DRAFT_PINS = [f for n, f in sorted(vars(TD).items()) if n.startswith("test_") and callable(f)]
+
+SOURCE_MUTANTS = {
+    "no_embedding_scale": ("w.input_embedding_scale * decode_rows(E", "decode_rows(E"),
+    "mask_slots_hold_anchor": ("tokens[:, 0] = anchors", "tokens[:, :] = np.asarray(anchors)[:, None]"),
+    "block_positions_from_zero": ("pos = np.asarray(ctx_lens, dtype=np.int64)[:, None] + np.arange(bs)[None, :]",
+                                  "pos = np.zeros((B, 1), dtype=np.int64) + np.arange(bs)[None, :]"),
+    "context_not_attended": ("o[b] = attention(q, np.concatenate([kc, kb]), np.concatenate([vc, vb]))",
+                             "o[b] = attention(q, kb, vb)"),
+    "attention_residual_dropped": ("h = h + linear(o, layer.wo)", "h = linear(o, layer.wo)"),
+    "ffn_residual_dropped": ("h = h + linear(act, layer.w_down)", "h = linear(act, layer.w_down)"),
+    "ffn_conv_skipped": ("h = conv(h, layer.conv_ffn, layer.dconv_ffn)", "h = h"),
+    "final_norm_skipped": ("nf = rmsnorm(h[:, 1:, :], decode(W.final_norm), w.rms_eps)", "nf = h[:, 1:, :]"),
+    "logits_from_wrong_slots": ("nf = rmsnorm(h[:, 1:, :]", "nf = rmsnorm(h[:, :-1, :]"),
+    "swiglu_halves_swapped": ("act = silu(gu[..., :w.ffn]) * gu[..., w.ffn:]",
+                              "act = silu(gu[..., w.ffn:]) * gu[..., :w.ffn]"),
+    "context_positions_shifted": ("pos[o0:o1] = int(ctx_lens[b]) - (o1 - o0) + np.arange(o1 - o0)",
+                                  "pos[o0:o1] = int(ctx_lens[b]) - (o1 - o0) + 1 + np.arange(o1 - o0)"),
+    "context_keys_unrotated": ("kk = rope(kv[:, :nkv * d].reshape(n_rows, nkv, d), pos, w.rope_theta)",
+                               "kk = kv[:, :nkv * d].reshape(n_rows, nkv, d)"),
+    "feature_norm_skipped": ("f = rmsnorm(linear(u, W.proj), decode(W.proj_norm), w.rms_eps)",
+                             "f = linear(u, W.proj)"),
+    "block_keys_unrotated": ("kb = rope(qkv[b, :, nq * d:(nq + nkv) * d].reshape(bs, nkv, d), pos[b], w.rope_theta)",
+                             "kb = qkv[b, :, nq * d:(nq + nkv) * d].reshape(bs, nkv, d)"),
+    "window_off_by_one": ("lo = max(0, L - w.sliding_window)", "lo = max(0, L - w.sliding_window + 1)"),
+}
+
+
+def _mutant_module(old, new):
+    assert _SRC.count(old) == 1, f"mutation site not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(_SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("mutant", sorted(SOURCE_MUTANTS))
+def test_composed_pins_catch_planted_mistake(mutant, monkeypatch):
+    m = _mutant_module(*SOURCE_MUTANTS[mutant])
+    for name in ("append_context", "draft_block", "step"):
+        monkeypatch.setattr(O, name, getattr(m, name))
+        monkeypatch.setattr(OD, name, getattr(m, name))
+    for pin in DRAFT_PINS:
+        try:
+            pin()
+        except AssertionError:
+            return
+    pytest.fail(f"no composed-forward pin noticed {mutant!r}")
+
+
+def test_composed_pins_pass_on_an_unmutated_copy(monkeypatch):
+    m = _mutant_module("def draft_block(", "def draft_block(")
+    for name in ("append_context", "draft_block", "step"):
+        monkeypatch.setattr(O, name, getattr(m, name))
+        monkeypatch.setattr(OD, name, getattr(m, name))
+    for pin in DRAFT_PINS:
+        pin()
