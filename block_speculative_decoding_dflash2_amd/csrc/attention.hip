@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256, (AttnShape<T, D>::OCC)) void attn_partial_kern
 }
 
 // One wave per (sequence, block row, q head): merge the chunk partials.
-// Lanes load the chunks' (max, sum) in parallel.  For the output, lane
+// Lanes read the chunks' (max, sum) in parallel.  For the output, lane
 // (cs, q) owns the 4 dimensions [4q, 4q + 4) and the chunks c = cs, cs + CS,
 // ... (CS = 64 / (d / 4) chunk subsets); the subsets are then added with
 // shuffles in a fixed order.
@@ -290,15 +290,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnCombineArgs p) {
   const int nvalid = (L < 0 || n_end <= lo_al) ? 0 : min(p.nchunks, (n_end - lo_al + CH - 1) / CH);
   const int64_t cbase = (int64_t(b) * p.nkv + g) * p.nchunks;
   const f32x2* ml = reinterpret_cast<const f32x2*>(p.part_ml);
-  float M = -INFINITY;
-  for (int c = lane; c < nvalid; c += WAVE) M = fmaxf(M, ml[(cbase + c) * QS + s][0]);
-  M = wave_max(M);
-  float lsum = 0.f;
-  for (int c = lane; c < nvalid; c += WAVE) {
-    const f32x2 v = ml[(cbase + c) * QS + s];
-    if (v[0] != -INFINITY) lsum += v[1] * exp2_safe(v[0] - M);
+  // up to 64 chunks: lane l reads chunk l's (max, sum) once and keeps it;
+  // more chunks: two passes (max, then the rescaled sums)
+  const bool one_pass = nvalid <= WAVE;
+  const f32x2 first = (one_pass && lane < nvalid) ? ml[(cbase + lane) * QS + s] : f32x2{-INFINITY, 0.f};
+  float M, lsum;
+  if (one_pass) {
+    M = wave_max(first[0]);
+    lsum = wave_sum(first[0] != -INFINITY ? first[1] * exp2_safe(first[0] - M) : 0.f);
+  } else {
+    float m = -INFINITY;
+    for (int c = lane; c < nvalid; c += WAVE) m = fmaxf(m, ml[(cbase + c) * QS + s][0]);
+    M = wave_max(m);
+    float l = 0.f;
+    for (int c = lane; c < nvalid; c += WAVE) {
+      const f32x2 v = ml[(cbase + c) * QS + s];
+      if (v[0] != -INFINITY) l += v[1] * exp2_safe(v[0] - M);
+    }
+    lsum = wave_sum(l);
   }
-  lsum = wave_sum(lsum);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 
   const int nq4 = p.d / 4;                  // 4 .. 64
@@ -306,11 +316,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnCombineArgs p) {
   const int q = lane % nq4, cs = lane / nq4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int cb = 0; cb < nvalid; cb += WAVE) {
-    float wgt = 0.f;
-    if (cb + lane < nvalid) {
-      const float mc = ml[(cbase + cb + lane) * QS + s][0];
-      wgt = mc != -INFINITY ? exp2_safe(mc - M) : 0.f;
-    }
+    float mc = first[0];
+    if (!one_pass) mc = cb + lane < nvalid ? ml[(cbase + cb + lane) * QS + s][0] : -INFINITY;
+    const float wgt = mc != -INFINITY ? exp2_safe(mc - M) : 0.f;
     const int n = min(WAVE, nvalid - cb);
     for (int c0 = 0; c0 < n; c0 += 4 * CS) {  // same trip count on every lane
       f32x4 v[4];
