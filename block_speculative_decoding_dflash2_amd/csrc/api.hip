@@ -301,13 +301,30 @@ dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weight
     return fail(DFLASH2_ERR_SHAPE, "create: mask_token_id %d outside [0, vocab)", c.mask_token_id);
   if (c.max_context < c.block_size)
     return fail(DFLASH2_ERR_SHAPE, "create: max_context %d < block_size", c.max_context);
-  if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f) || !(c.final_logit_softcapping >= 0.f))
+  if (!(c.rms_eps >= 0.f) || !std::isfinite(c.rms_eps) || !(c.rope_theta > 0.f) ||
+      !std::isfinite(c.rope_theta) || !(c.final_logit_softcapping >= 0.f) ||
+      !std::isfinite(c.final_logit_softcapping))
     return fail(DFLASH2_ERR_INVALID_ARG, "create: bad rms_eps / rope_theta / softcap");
+  // Top-k ranks the raw logits and the transform is applied to the k kept
+  // values, which is the top-k of the transformed logits only while the
+  // transform is strictly increasing: the multiplier must be positive.
+  if (!(c.output_multiplier > 0.f) || !std::isfinite(c.output_multiplier))
+    return fail(DFLASH2_ERR_INVALID_ARG, "create: output_multiplier %g must be finite and > 0",
+                double(c.output_multiplier));
+  if (!std::isfinite(c.input_embedding_scale))
+    return fail(DFLASH2_ERR_INVALID_ARG, "create: input_embedding_scale is not finite");
   if (!attn_supported(c.head_dim))
     return fail(DFLASH2_ERR_UNSUPPORTED, "create: head_dim %d not in {16, 32, 64, 128, 256}",
                 c.head_dim);
-  const int qd = c.num_q_heads * c.head_dim;
-  if (c.hidden % 32 || c.ffn % 32 || qd % 32 || (c.num_taps * c.tap_width) % 32)
+  // The GEMMs address a tile of at most 128 rows with 32-bit byte offsets
+  // from a 64-bit tile base: every contraction length stays <= 2^20.
+  constexpr int64_t kMaxContraction = int64_t(1) << 20;
+  const int64_t qd = int64_t(c.num_q_heads) * c.head_dim;
+  const int64_t kp = int64_t(c.num_taps) * c.tap_width;
+  if (c.ffn > kMaxContraction || qd > kMaxContraction || kp > kMaxContraction)
+    return fail(DFLASH2_ERR_UNSUPPORTED,
+                "create: ffn, nq*head_dim and num_taps*tap_width must be <= 1048576");
+  if (c.hidden % 32 || c.ffn % 32 || qd % 32 || kp % 32)
     return fail(DFLASH2_ERR_UNSUPPORTED,
                 "create: hidden, ffn, nq*head_dim and num_taps*tap_width must be multiples of 32");
   if (c.hidden > 16384) return fail(DFLASH2_ERR_UNSUPPORTED, "create: hidden > 16384");

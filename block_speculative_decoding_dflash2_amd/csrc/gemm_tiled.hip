@@ -115,17 +115,22 @@ struct TiledMain {
     constexpr int LPR = 64 * SW / 16;          // lanes per row in a coalesced load (8 bf16, 4 fp8)
     constexpr int RPI = 64 / LPR;              // rows per load instruction
     const int xr = tid >> 3, xc = tid & 7;
-    const char* wbase = reinterpret_cast<const char*>(W);
-    const char* xbase = reinterpret_cast<const char*>(X);
+    // 64-bit bases at the first row of the wave's weight rows and of the
+    // block's activation rows (and at k = kb); the per-lane offsets from
+    // them stay below 2^32 bytes because a tile spans at most 128 rows of at
+    // most 2^20 elements (both checked when the handle is created)
+    const int wb0 = min(n0w, N - 1), xb0 = min(m0, Mact - 1);
+    const char* wbase = reinterpret_cast<const char*>(W) + (int64_t(wb0) * ldw + kb) * SW;
+    const char* xbase = reinterpret_cast<const char*>(X) + (int64_t(xb0) * ldx + kb) * 2;
     // coalesced weight loads: instruction q covers rows RPI q .. RPI q + RPI - 1 of the wave's 64
     const int wrow = lane / LPR, wcol = lane % LPR;
     uint32_t woffc[NLD], xoffc[XQ];
 #pragma unroll
     for (int q = 0; q < NLD; ++q)
-      woffc[q] = uint32_t(min(n0w + RPI * q + wrow, N - 1)) * uint32_t(ldw) * SW + uint32_t(kb * SW + 16 * wcol);
+      woffc[q] = uint32_t(min(n0w + RPI * q + wrow, N - 1) - wb0) * uint32_t(ldw) * SW + uint32_t(16 * wcol);
 #pragma unroll
     for (int q = 0; q < XQ; ++q)
-      xoffc[q] = (uint32_t(min(m0 + xr + 32 * q, Mact - 1)) * uint32_t(ldx) + uint32_t(kb + 8 * xc)) * 2u;
+      xoffc[q] = (uint32_t(min(m0 + xr + 32 * q, Mact - 1) - xb0) * uint32_t(ldx) + uint32_t(8 * xc)) * 2u;
     char* xdst = lds + xr * kTXRow + 16 * xc;
     const char* xsrc = lds + r * kTXRow + 16 * h;
     char* wl = lds + 2 * XBUF + wave * WBUF;

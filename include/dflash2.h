@@ -103,9 +103,12 @@ typedef struct {
                                (dconv_attn/dconv_ffn); must divide hidden   */
   float rms_eps;            /* RMSNorm epsilon                                */
   float rope_theta;         /* RoPE base                                      */
-  float input_embedding_scale;   /* scales the embedded block (1 = identity)  */
-  float output_multiplier;       /* logit transform multiplier (1 = identity) */
-  float final_logit_softcapping; /* logit soft cap; 0 = off                   */
+  float input_embedding_scale;   /* scales the embedded block (1 = identity);
+                                    must be finite                             */
+  float output_multiplier;       /* logit transform multiplier (1 = identity);
+                                    must be finite and > 0, so that the
+                                    transform keeps the ranking of the logits */
+  float final_logit_softcapping; /* logit soft cap; 0 = off; finite, >= 0      */
 } dflash2_config;
 
 /* Per-layer weights [device].  *_scale are float32 [out rows], required for
@@ -162,11 +165,15 @@ typedef struct dflash2_handle dflash2_handle;
  * divide hidden, selector_top_k outside 1..min(64, vocab), selector_rank
  * outside 1..256, mask_token_id outside [0, vocab), an unknown weight_dtype,
  * a null weight (the static conv taps when conv_group_size is 0, the dynamic
- * ones otherwise), a missing fp8 scale, and (UNSUPPORTED) any contraction
+ * ones otherwise), a missing fp8 scale, a non-finite rms_eps, rope_theta,
+ * input_embedding_scale or softcap, an output_multiplier that is not finite
+ * and > 0 (top-k ranks the raw logits and transforms the kept values, which
+ * needs a strictly increasing transform), and (UNSUPPORTED) any contraction
  * length (hidden, ffn, nq*head_dim, num_taps*tap_width) that is not a
- * multiple of 32, hidden > 16384 or max_context not a multiple of 8.  The handle keeps a host copy of the config and the
- * pointer table only; it is immutable and may be shared across threads and
- * streams. */
+ * multiple of 32 or exceeds 2^20 (the GEMM tiles use 32-bit offsets from a
+ * 64-bit tile base), hidden > 16384 or max_context not a multiple of 8.  The
+ * handle keeps a host copy of the config and the pointer table only; it is
+ * immutable and may be shared across threads and streams. */
 dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weights* weights,
                               dflash2_handle** out);
 void dflash2_destroy(dflash2_handle* handle);

@@ -82,6 +82,27 @@ BASE = synth.get("tiny_fp32").abi_config()
     ({"max_context": 36}, L.DFLASH2_ERR_UNSUPPORTED),
     ({"max_context": 4}, L.DFLASH2_ERR_SHAPE),
     ({"selector_top_k": 64, "selector_rank": 256}, L.DFLASH2_OK),   # the largest selector fits LDS
+    # the logit transform must be strictly increasing (top-k ranks the raw logits)
+    ({"output_multiplier": 0.0}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"output_multiplier": -0.5}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"output_multiplier": float("nan")}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"output_multiplier": float("inf")}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"output_multiplier": 0.5, "final_logit_softcapping": 30.0, "input_embedding_scale": 2.5}, L.DFLASH2_OK),
+    ({"input_embedding_scale": float("nan")}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"input_embedding_scale": float("-inf")}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"input_embedding_scale": -1.0}, L.DFLASH2_OK),
+    ({"final_logit_softcapping": float("inf")}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"final_logit_softcapping": -1.0}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"rms_eps": float("nan")}, L.DFLASH2_ERR_INVALID_ARG),
+    ({"rope_theta": float("inf")}, L.DFLASH2_ERR_INVALID_ARG),
+    # contraction lengths: the GEMM tiles address at most 128 rows of 2^20
+    # elements with 32-bit offsets from a 64-bit tile base
+    ({"ffn": 1 << 20}, L.DFLASH2_OK),
+    ({"ffn": (1 << 20) + 32}, L.DFLASH2_ERR_UNSUPPORTED),
+    ({"num_taps": 33, "tap_width": 1 << 15}, L.DFLASH2_ERR_UNSUPPORTED),
+    ({"num_taps": 32, "tap_width": 1 << 15}, L.DFLASH2_OK),
+    ({"num_q_heads": 8193, "num_kv_heads": 1, "head_dim": 128}, L.DFLASH2_ERR_UNSUPPORTED),
+    ({"num_taps": 1 << 16, "tap_width": 1 << 16}, L.DFLASH2_ERR_UNSUPPORTED),  # product overflows int32
 ])
 def test_create_validation(change, status):
     cfg = dict(BASE, **change)
@@ -168,6 +189,17 @@ def test_verify_argument_errors():
     with pytest.raises(L.DFlash2Error) as e:
         L.dflash2_verify_accept(None, 4, 8, 1000, p, p, p, p, None, p, n - 8)
     assert e.value.status == L.DFLASH2_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("vocab,hidden,dtype", [(262144, 8192, "bf16"), (151936, 16384, "bf16"),
+                                                (270000, 8192, "bf16"), (262144, 16384, "fp8")])
+def test_create_accepts_lm_head_beyond_4gib(vocab, hidden, dtype):
+    """lm_head weights of 4 GiB and more (V * H * bytes >= 2^32) are valid:
+    the tiled GEMMs form 64-bit tile bases, so no offset wraps inside the
+    weight (the GPU side is checked by test_lmhead_tiled_beyond_4gib)."""
+    cfg = dict(BASE, vocab=vocab, hidden=hidden, mask_token_id=vocab - 1, weight_dtype=dtype)
+    assert vocab * hidden * (1 if dtype == "fp8" else 2) >= 1 << 32
+    assert _status_create(cfg) == L.DFLASH2_OK, L.dflash2_last_error()
 
 
 def test_full_workload_configs_validate():

@@ -74,9 +74,22 @@ def check_step(g: DraftRun, res, seqs):
     delta = float(np.max(np.abs(glog.astype(np.float64) - res["zeta"])))
     log(f"{w.name}: err cache {e_cache:.2e} hidden {e_hidden:.2e} logits {e_logit:.2e} (delta {delta:.2e})")
     assert e_cache <= tol and e_hidden <= tol and e_logit <= tol
-    # 3. the GPU's top-k is the top-k of its own logits
-    assert topk_consistent(g.topk_ids[seqs].reshape(-1, k), g.topk_vals[seqs].reshape(-1, k),
-                           glog.reshape(-1, w.vocab), k)
+    # 3. the GPU's top-k is the top-k of its own logits; its values are the
+    # transformed logits (output_multiplier, then the soft cap) at those ids
+    ids = g.topk_ids[seqs].reshape(-1, k)
+    vals = g.topk_vals[seqs].reshape(-1, k)
+    z_own = glog.reshape(-1, w.vocab)
+    raw = np.take_along_axis(z_own, ids.astype(np.int64), axis=1)
+    assert topk_consistent(ids, raw, z_own, k)
+    mult, cap = w.output_multiplier, w.final_logit_softcapping
+    if mult == 1.0 and cap == 0.0:
+        assert np.array_equal(vals, raw + np.float32(0.0))
+    else:
+        # float32 multiply and tanhf on the GPU against float64: a few ulp
+        want_t = O.logit_transform(raw.astype(np.float64), mult, cap)
+        e_t = float(np.max(np.abs(vals - want_t)))
+        log(f"{w.name}: transformed top-k values off by {e_t:.2e} (multiplier {mult}, cap {cap})")
+        assert e_t <= 8 * np.finfo(np.float32).eps * max(1.0, float(np.max(np.abs(want_t))))
     # 4. candidate sets where the oracle's boundary gap exceeds 2 delta
     z32 = res["zeta"].astype(np.float32).reshape(len(seqs), P, -1)
     srt = -np.sort(-z32.astype(np.float64), axis=-1)
@@ -85,6 +98,16 @@ def check_step(g: DraftRun, res, seqs):
     same_set = np.array([[set(g.topk_ids[b, t].tolist()) == set(res["topk_ids"][i, t].tolist())
                           for t in range(P)] for i, b in enumerate(seqs)])
     assert same_set[qual].all(), f"candidate sets differ at {np.argwhere(qual & ~same_set)}"
+    # ... and there the (transformed) candidate values, the selector's unary
+    # term, agree with the oracle's within the logit tolerance
+    same_ids = np.array([[np.array_equal(g.topk_ids[b, t], res["topk_ids"][i, t]) for t in range(P)]
+                         for i, b in enumerate(seqs)])
+    if same_ids.any():
+        gv = g.topk_vals[seqs][same_ids]
+        ov = res["topk_vals"][same_ids]
+        e_vals = normwise(gv, ov)
+        log(f"{w.name}: top-k values error {e_vals:.2e} on {same_ids.mean():.3f} of the positions")
+        assert e_vals <= tol
     # 5. drafts where the max-sum decision margin is clear
     margins = _through_margins(res["pair"], res["topk_vals"], res["path"])
     seq_ok = qual.all(axis=1)
@@ -115,6 +138,61 @@ def test_draft_small_workloads(name):
     try:
         _, res = oracle_for(w, g.W)
         check_step(g, res, range(w.batch))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "medium_fp8", "small_fp32"])
+def test_draft_embedding_scale_and_logit_transform(name):
+    """input_embedding_scale = 2.5 on the embedded block, and the logit
+    transform output_multiplier = 0.5 then final_logit_softcapping = 30 on
+    the candidates (NeMo AutoModel page, Key Config Fields): small_bf16 and
+    small_fp32 take the weight-streaming lm_head (at most 64 rows), medium_fp8
+    the LDS-tiled one.  Hidden states, logits, appended rows and the
+    transformed top-k values are checked against the oracle, the drafts where
+    the decision margins are clear.  A transform applied in the other order
+    (cap, then multiplier) moves the values by far more than the bound."""
+    w = synth.get(name).replace(input_embedding_scale=2.5, output_multiplier=0.5,
+                                final_logit_softcapping=30.0, name=f"{name}_transform")
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+        # the swapped order gives values that differ from the stored ones
+        raw = np.take_along_axis(g.logits.reshape(-1, w.vocab), g.topk_ids.reshape(-1, w.top_k).astype(np.int64),
+                                 axis=1).astype(np.float64)
+        swapped = 0.5 * (30.0 * np.tanh(raw / 30.0))
+        assert np.max(np.abs(swapped - g.topk_vals.reshape(-1, w.top_k))) > 1e-4
+    finally:
+        g.close()
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_lmhead_tiled_beyond_4gib():
+    """A bf16 lm_head of 270000 x 8192 (4.1 GiB, rows 262144 and up start
+    past 2^32 bytes) on the tiled path (70 rows): the logits of ids past the
+    4 GiB line, and a sample below it, equal the float64 product of the GPU's
+    own final hidden states (RMSNorm, gain) with those lm_head rows, and the
+    top-k is the top-k of the GPU's own logits."""
+    w = synth.get("small_bf16").replace(
+        name="wide_vocab_bf16", index=15, batch=10, block_size=8, hidden=8192, num_layers=1,
+        num_q_heads=2, num_kv_heads=1, head_dim=64, ffn=64, vocab=270000, num_taps=1, tap_width=64,
+        ctx=(16, 16), top_k=4, rank=8)
+    assert w.vocab * w.hidden * 2 > (1 << 32) and w.batch * (w.block_size - 1) > 64
+    g = DraftRun(w)
+    try:
+        V, H = w.vocab, w.hidden
+        z = g.logits.reshape(-1, V)
+        h = g.hidden[:, 1:, :].reshape(-1, H).astype(np.float64)
+        nf = O.rmsnorm(h, O.decode(g.W.final_norm), w.rms_eps)
+        rng = np.random.default_rng(0)
+        cols = np.unique(np.concatenate([np.arange(262144 - 64, V), rng.integers(0, 262144, 512)]))
+        want = nf @ O.bf16_bits_to_f64(g.W.lm_head.data[cols]).T
+        err = normwise(z[:, cols], want)
+        log(f"wide vocab: logits error {err:.2e} over {len(cols)} ids ({np.sum(cols >= 262144)} past 4 GiB)")
+        assert err <= TOL["bf16"]
+        assert topk_consistent(g.topk_ids.reshape(-1, w.top_k), g.topk_vals.reshape(-1, w.top_k), z, w.top_k)
     finally:
         g.close()
 
