@@ -87,6 +87,8 @@ def _load():
                                    c_float, i32p, i32p, f32p, vp, c_size_t], c_int32),
         "dflash2_verify_accept": ([vp, c_int32, c_int32, c_int32, i32p, f32p, i32p, i32p, i32p, vp,
                                    c_size_t], c_int32),
+        "dflash2_verify_accept_noalloc": ([vp, c_int32, c_int32, c_int32, i32p, f32p, i32p, i32p, i32p],
+                                          c_int32),
         "dflash2_draft_losses_workspace_size": ([c_int32, c_int32, c_int32, POINTER(c_size_t)], c_int32),
         "dflash2_draft_losses": ([vp, vp, c_int32, i32p, i32p, f32p, i32p, f32p, c_float, c_float, f32p, f32p,
                                   f32p, vp, c_size_t], c_int32),
@@ -104,7 +106,8 @@ def _load():
 lib = _load()
 EXPORTED = ("dflash2_create", "dflash2_destroy", "dflash2_workspace_size", "dflash2_draft_block",
             "dflash2_select_path", "dflash2_select_path_stop", "dflash2_verify_workspace_size",
-            "dflash2_verify_accept", "dflash2_verify_sample_workspace_size", "dflash2_verify_sample",
+            "dflash2_verify_accept", "dflash2_verify_accept_noalloc", "dflash2_verify_sample_workspace_size",
+            "dflash2_verify_sample",
             "dflash2_draft_losses_workspace_size", "dflash2_draft_losses",
             "dflash2_trace_attach", "dflash2_trace_detach", "dflash2_last_error")
 
@@ -166,6 +169,12 @@ def dflash2_verify_accept(stream, batch, block_size, vocab, draft_tokens, target
                           bonus, target_argmax, workspace, workspace_bytes) -> None:
     _check(lib.dflash2_verify_accept(stream, batch, block_size, vocab, draft_tokens, target_logits,
                                      accepted, bonus, target_argmax, workspace, workspace_bytes))
+
+
+def dflash2_verify_accept_noalloc(stream, batch, block_size, vocab, draft_tokens, target_logits, accepted,
+                                  bonus, target_argmax) -> None:
+    _check(lib.dflash2_verify_accept_noalloc(stream, batch, block_size, vocab, draft_tokens, target_logits,
+                                             accepted, bonus, target_argmax))
 
 
 def dflash2_select_path_stop(handle, stream, batch, anchor_ids, topk_ids, topk_vals, p_min, n_min, n_max,

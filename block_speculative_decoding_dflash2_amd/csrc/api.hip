@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -749,6 +750,74 @@ dflash2_status dflash2_verify_accept(hipStream_t stream, int32_t batch, int32_t 
     return fail(DFLASH2_ERR_WORKSPACE, "verify_accept: workspace needs %zu bytes, 256-aligned", vp.bytes);
   const dflash2_status st = greedy_impl(stream, batch, block_size, vocab, draft_tokens, nullptr, target_logits,
                                         accepted, bonus, target_argmax, nullptr, workspace, "verify_accept");
+  return st == DFLASH2_OK ? ok() : st;
+}
+
+}  // extern "C"
+
+// Scratch of dflash2_verify_accept_noalloc: the per-(row, vocabulary chunk)
+// best keys of the greedy verifier, held in this library's own device array
+// instead of a caller workspace.  Each GPU holds its own copy for the life
+// of the process; every call on a GPU shares it, so calls that overlap on
+// one GPU race.  The verifier overwrites every key it reads back, so
+// nothing needs clearing between calls.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the stream's device, looked up once per
+// device with that device current (the host-side name is not a device
+// address).
+dflash2_status scratch_address(hipStream_t stream, void** out, const char* name) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DFLASH2_ERR_HIP, "%s: device of the stream: %s", name, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DFLASH2_ERR_HIP, "%s: device %d out of range", name, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int prev = 0;
+    if ((e = hipGetDevice(&prev)) != hipSuccess)
+      return fail(DFLASH2_ERR_HIP, "%s: hipGetDevice: %s", name, hipGetErrorString(e));
+    if (prev != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(DFLASH2_ERR_HIP, "%s: hipSetDevice(%d): %s", name, dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev != dev) (void)hipSetDevice(prev);
+    if (e != hipSuccess || !p)
+      return fail(DFLASH2_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", name, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DFLASH2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dflash2_status dflash2_verify_accept_noalloc(hipStream_t stream, int32_t batch, int32_t block_size,
+                                             int32_t vocab, const int32_t* draft_tokens,
+                                             const float* target_logits, int32_t* accepted,
+                                             int32_t* bonus, int32_t* target_argmax) {
+  if (batch < 1 || block_size < 2 || vocab < 1)
+    return fail(DFLASH2_ERR_SHAPE, "verify_accept_noalloc: bad sizes (batch %d, block_size %d, vocab %d)",
+                batch, block_size, vocab);
+  if (!draft_tokens || !target_logits || !accepted || !bonus)
+    return fail(DFLASH2_ERR_INVALID_ARG, "verify_accept_noalloc: null pointer argument");
+  const VerifyPlan vp = plan_verify(batch, block_size, vocab);
+  if (vp.bytes > kNoAllocScratchBytes)
+    return fail(DFLASH2_ERR_WORKSPACE,
+                "verify_accept_noalloc: needs %zu bytes of scratch, more than its built-in %zu "
+                "(batch * block_size <= %zu); use dflash2_verify_accept with a workspace",
+                vp.bytes, kNoAllocScratchBytes, kNoAllocScratchBytes / 8);
+  void* ws = nullptr;
+  dflash2_status st = scratch_address(stream, &ws, "verify_accept_noalloc");
+  if (st != DFLASH2_OK) return st;
+  st = greedy_impl(stream, batch, block_size, vocab, draft_tokens, nullptr, target_logits, accepted, bonus,
+                   target_argmax, nullptr, ws, "verify_accept_noalloc");
   return st == DFLASH2_OK ? ok() : st;
 }
 

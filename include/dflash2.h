@@ -286,6 +286,22 @@ dflash2_status dflash2_verify_accept(hipStream_t stream, int32_t batch, int32_t 
                                      int32_t* bonus, int32_t* target_argmax, void* workspace,
                                      size_t workspace_bytes);
 
+/* For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): dflash2_verify_accept with its scratch in a fixed device
+ * array inside the library (1 MiB per GPU, held until the process ends)
+ * instead of a workspace argument.  Same arguments, kernels and results as
+ * dflash2_verify_accept.  batch * block_size must be <= 131072, else
+ * DFLASH2_ERR_WORKSPACE (before any device work).  The array's device
+ * address is looked up once per GPU, on the first call with a stream of
+ * that GPU; no call allocates.  All calls on one GPU share the array:
+ * calls that overlap on one GPU (concurrent streams or threads) race, and
+ * must be serialised by the caller. */
+dflash2_status dflash2_verify_accept_noalloc(hipStream_t stream, int32_t batch, int32_t block_size,
+                                             int32_t vocab, const int32_t* draft_tokens,
+                                             const float* target_logits, int32_t* accepted,
+                                             int32_t* bonus, int32_t* target_argmax);
+
 /* Bytes of device workspace dflash2_verify_sample needs (>= the greedy
  * verification's). */
 dflash2_status dflash2_verify_sample_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,

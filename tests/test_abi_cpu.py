@@ -202,6 +202,25 @@ def test_create_accepts_lm_head_beyond_4gib(vocab, hidden, dtype):
     assert _status_create(cfg) == L.DFLASH2_OK, L.dflash2_last_error()
 
 
+def test_verify_noalloc_argument_errors():
+    """The allocation-free verifier rejects bad sizes, null pointers and
+    batches whose scratch exceeds its fixed 1 MiB (batch * block_size >
+    131072) before any device work."""
+    p = 0x1000
+    with pytest.raises(L.DFlash2Error) as e:
+        L.dflash2_verify_accept_noalloc(None, 4, 1, 1000, p, p, p, p, None)
+    assert e.value.status == L.DFLASH2_ERR_SHAPE
+    with pytest.raises(L.DFlash2Error) as e:
+        L.dflash2_verify_accept_noalloc(None, 4, 8, 1000, p, p, None, p, None)
+    assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
+    with pytest.raises(L.DFlash2Error) as e:
+        L.dflash2_verify_accept_noalloc(None, 16385, 8, 1000, p, p, p, p, None)
+    assert e.value.status == L.DFLASH2_ERR_WORKSPACE
+    assert "131072" in L.dflash2_last_error()
+    # the largest accepted batch needs exactly the built-in 1 MiB
+    assert L.dflash2_verify_workspace_size(16384, 8, 151936) == 1 << 20
+
+
 def test_full_workload_configs_validate():
     for name in synth.WORKLOADS:
         cfg = synth.get(name).abi_config()
