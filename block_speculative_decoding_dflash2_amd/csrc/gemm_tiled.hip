@@ -18,9 +18,10 @@
 // each XCD (blocks go to the 8 XCDs round-robin) runs a contiguous run of
 // tile numbers: the blocks that share a weight tile share that XCD's L2.
 //
-// Two epilogues: float32 split-K partial sums (the same layout the
-// weight-streaming kernels write, reduced by the consumer kernel), and the
-// lm_head's per-256-vocabulary-group top-k (see the top-k section below).
+// Epilogues: float32 split-K partial sums (the same layout the
+// weight-streaming kernels write, reduced by the consumer kernel), or with
+// one K split the consumer itself (SwiGLU, or RoPE and the cache stores).
+// The lm_head of many rows has its own kernel (lmhead_tiled.hip).
 #include <algorithm>
 #include <cstdlib>
 
@@ -33,7 +34,6 @@ namespace {
 constexpr int kTBN = 256;            // weight rows per block (64 per wave)
 constexpr int kTKT = 64;             // contraction depth per LDS stage
 constexpr int kTXRow = kTKT * 2 + 16;  // LDS bytes per activation row
-constexpr int kTSlots = 32;          // top-k candidate slots per row and round
 // Buffer resource word 3 for untyped 32-bit data on gfx9-family chips.
 constexpr int kBufferFlags = 0x00020000;
 }  // namespace
@@ -51,9 +51,7 @@ struct TiledArgs {
   const float* Sg[kMaxGroups];
   int64_t group_stride;
   float* P; int64_t ldp, split_stride;       // partial-sum epilogue
-  int k, vgroups; uint64_t* cand; float* debug_logits;  // top-k epilogue
   int nM, nN, tiles;
-  int tpb;                                    // vocabulary tiles per lm_head block
   GemmEpi epi;                                // gemm_tiled_kernel consumer (one K split)
 };
 
@@ -448,312 +446,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// lm_head + top-k.  A block owns BM rows and a run of consecutive 256-id
-// vocabulary tiles [nt0, nt1); for each row it keeps the 16 best keys
-// (value desc, id asc) seen so far in its output slot cand[m][range][0..16),
-// which the merge kernel reduces to each row's final k.
-//
-// Per tile, only values that can still enter a row's list are looked at:
-//  * first tile: a lane holds 32 values of each of its rows in two groups of
-//    16 (one per 32-row weight fragment) and keeps the largest and second
-//    largest of each; the row's 16 groups give 32 such values, and their
-//    16th largest, T, has at least 16 of the row's values >= T, so nothing
-//    below T can be in the row's top 16;
-//  * later tiles: the row's current 16th key;
-// values passing (typically ~18 of 256 on the first tile, a few on later
-// ones) are compacted into the row's candidate slots in LDS (one atomic per
-// lane and row), and the thread owning the row insertion-sorts them into its
-// list.  If a row had more than kTSlots passing values, further rounds take
-// the values not yet appended whose key beats the row's new 16th key.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void sort16_desc(float (&a)[16]) {
-#pragma unroll
-  for (int size = 2; size <= 16; size <<= 1)
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int l = i ^ stride;
-        if (l > i) {
-          const bool desc = (i & size) == 0;
-          const float hi = fmaxf(a[i], a[l]), lo = fminf(a[i], a[l]);
-          a[i] = desc ? hi : lo;
-          a[l] = desc ? lo : hi;
-        }
-      }
-}
-
-__device__ __forceinline__ void insert16(uint64_t (&L)[16], uint64_t x) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const bool c = x > L[i];
-    const uint64_t t = L[i];
-    L[i] = c ? x : t;
-    x = c ? t : x;
-  }
-}
-
-template <typename TW, int FM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_tiled_kernel(TiledArgs p) {
-  typedef TiledMain<TW, FM> Main;
-  constexpr int BM = Main::BM, F2 = Main::F2;
-  constexpr int XB = Main::LDS_BYTES;
-  constexpr int CB = BM * kTSlots * 8;   // candidate slots
-  constexpr int SB = 4 * WAVE * 36 * 4;  // per-wave staging of one row's 32 values per lane (append)
-  constexpr int TB = 64 * 260 * 4;       // 64 rows of tile values (overflow path)
-  constexpr int CSB = CB + SB;
-  constexpr int LB = XB > CSB ? (XB > TB ? XB : TB) : (CSB > TB ? CSB : TB);
-  __shared__ __attribute__((aligned(16))) char lds[LB];
-  __shared__ float inv[BM];
-  __shared__ float thr[BM];       // first tile: float bound T
-  __shared__ uint64_t thrk[BM];   // the row's current 16th key (0: list not full)
-  __shared__ int cnt[BM];
-  // block -> (row tile, vocabulary range); blocks of one range are adjacent
-  const int per = gridDim.x >> 3;
-  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (t >= p.tiles) return;
-  const int mt = t % p.nM, rg = t / p.nM;
-  const int nt0 = rg * p.tpb, nt1 = min(p.nN, nt0 + p.tpb);
-  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
-  const int m0 = mt * BM;
-  if (m0 >= Mact) return;
-  const int tid = threadIdx.x, wave = tid / WAVE, lane = tid & (WAVE - 1);
-  const int r = lane & 31, h = lane >> 5;
-  tiled_row_scales<BM>(p.rs, m0, Mact, inv);
-  if (tid < BM) {
-    thrk[tid] = 0ull;
-    cnt[tid] = 0;
-  }
-  const bool owner = tid < BM && m0 + tid < Mact;
-  static_assert(2 * BM == 256, "two threads per row in the ranking steps");
-  uint64_t* slots = reinterpret_cast<uint64_t*>(lds);
-
-  for (int nt = nt0; nt < nt1; ++nt) {
-    const int n0w = nt * kTBN + 64 * wave;
-    const bool first = nt == nt0;
-    f32x16 acc[2][F2];
-    Main::run(p.X, p.ldx, static_cast<const TW*>(p.W), p.ldw, p.N, Mact, n0w, m0, 0, p.K / kTKT, acc, lds);
-    __syncthreads();  // every wave is done with the stages; LDS is free
-
-    // logits (the same float32 steps as the weight-streaming lm_head); value
-    // v = 4 q + e of acc[i][j] is vocabulary id n0w + 32 i + 8 q + 4 h + e of
-    // row m0 + 32 j + r.  Ids past the vocabulary become NaN, which passes no
-    // filter below.
-    float* ab = reinterpret_cast<float*>(lds);  // [BM][33]: per-group top-2 of each row
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      float s[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        s[v] = p.scale ? p.scale[min(n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3), p.N - 1)] : 1.f;
-#pragma unroll
-      for (int j = 0; j < F2; ++j) {
-        const float iv = inv[32 * j + r];
-        const int m = m0 + 32 * j + r;
-        float a = -INFINITY, b = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = acc[i][j][v];
-          x *= s[v];
-          x *= iv;
-          x = x + 0.0f;
-          const bool valid = n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3) < p.N;
-          const float y = valid ? x : -INFINITY;
-          b = fmaxf(b, fminf(a, y));
-          a = fmaxf(a, y);
-          acc[i][j][v] = valid ? x : __builtin_nanf("");
-        }
-        if (p.debug_logits && m < Mact) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int nb = n0w + 32 * i + 8 * q + 4 * h;
-            float* dst = p.debug_logits + int64_t(m) * p.N + nb;
-            if (nb + 3 < p.N && (p.N & 3) == 0) {
-              *reinterpret_cast<f32x4*>(dst) =
-                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (nb + e < p.N) dst[e] = acc[i][j][4 * q + e];
-            }
-          }
-        }
-        if (first) {
-          const int slot = ((wave * 2 + h) * 2 + i) * 2;
-          ab[(32 * j + r) * 33 + slot] = a;
-          ab[(32 * j + r) * 33 + slot + 1] = b;
-        }
-      }
-    }
-    if (first) {
-      // two adjacent lanes per row: one sorts the group maxima A, the other
-      // the second maxima B; the 16 largest of the union are
-      // max(A[q], B[15 - q]), and T is their minimum
-      __syncthreads();
-      const int row = tid >> 1, half = tid & 1;
-      float L[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) L[q] = ab[row * 33 + 2 * q + half];
-      sort16_desc(L);
-      float T = INFINITY;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) T = fminf(T, fmaxf(L[q], __shfl_xor(L[15 - q], 1, WAVE)));
-      if (half == 0) thr[row] = T;
-    }
-    __syncthreads();  // ab is dead from here; its space holds the candidate slots
-
-    // append the lane's passing values of each of its rows: one atomic per
-    // row for the lane's count, then the keys at consecutive slots.  The
-    // lane's 32 values of a row are staged in its own LDS row so that only
-    // the set bits of its mask are visited (a short divergent loop) instead
-    // of testing all 32 values with a branch each.
-    float* vstage = reinterpret_cast<float*>(lds + CB) + (wave * WAVE + lane) * 36;
-    auto append = [&](const uint32_t (&mask)[F2]) {
-      int base[F2];
-#pragma unroll
-      for (int j = 0; j < F2; ++j) {
-        const int c = __builtin_popcount(mask[j]);
-        base[j] = c ? atomicAdd(&cnt[32 * j + r], c) : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < F2; ++j) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<f32x4*>(vstage + 16 * i + 4 * q) =
-                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        uint32_t m = mask[j];
-        int pos = base[j];
-        uint64_t* dst = slots + (32 * j + r) * kTSlots;
-        while (m != 0u && pos < kTSlots) {
-          const int bit = __builtin_ctz(m);
-          m &= m - 1u;
-          const int v = bit & 15;
-          const uint32_t id = uint32_t(n0w + 32 * (bit >> 4) + 8 * (v >> 2) + 4 * h + (v & 3));
-          dst[pos] = rank_key(vstage[bit], id);
-          ++pos;
-        }
-      }
-    };
-    {
-      uint32_t mask[F2];
-#pragma unroll
-      for (int j = 0; j < F2; ++j) {
-        const int row = 32 * j + r;
-        const float tf = thr[row];
-        const uint64_t tk = thrk[row];
-        const float tv = key_val(tk);
-        const uint32_t tlo = uint32_t(tk);
-        mask[j] = 0u;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float x = acc[i][j][v];
-            const uint32_t nid = uint32_t(n0w + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3));
-            bool pass;
-            if (first) pass = x >= tf;
-            else pass = tk == 0ull ? x == x : (x > tv || (x == tv && 0xFFFFFFFFu - nid > tlo));
-            mask[j] |= uint32_t(pass) << (16 * i + v);
-          }
-      }
-      append(mask);
-    }
-    // merge the row's new candidates into its list (kept in its output slot)
-    // (two adjacent lanes per row: each inserts every other candidate, the
-    // first also the row's list so far, then the two lists are merged)
-    auto merge = [&](bool fresh) {
-      const int row = tid >> 1, half = tid & 1;
-      const bool own = m0 + row < Mact;
-      uint64_t* o = p.cand + (int64_t(min(m0 + row, p.M - 1)) * p.vgroups + rg) * 16;
-      uint64_t list[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) list[q] = (!fresh && own && half == 0) ? o[q] : 0ull;
-      const int c = cnt[row];
-      const int nn = min(c, kTSlots);
-      for (int q = half; q < nn; q += 2) insert16(list, slots[row * kTSlots + q]);
-      uint64_t brev[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) brev[q] = __shfl_xor(list[15 - q], 1, WAVE);
-      bitonic_top<16>(list, brev);
-      bool more = false;
-      if (half == 0) {
-        if (own) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) o[q] = list[q];
-        }
-        // rows past the last activation row are never output: stop them here
-        more = own && c > kTSlots;
-        thrk[row] = own ? list[15] : ~0ull;
-        cnt[row] = 0;
-      }
-      return more;
-    };
-    // common case: no row overflowed, the tile's values are dead before the merge
-    if (!__syncthreads_or(owner && cnt[tid] > kTSlots)) {
-      merge(first);
-    } else {
-      // rare: a row had more than kTSlots values past its bound.  Rank every
-      // value of the tile exactly instead, 64 rows at a time through LDS,
-      // four threads per row, and fold the result into the rows' lists.
-      float* tv = reinterpret_cast<float*>(lds);  // [64][260]
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < F2; ++j) {
-          if ((j >> 1) != half) continue;
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              tv[(32 * (j & 1) + r) * 260 + 64 * wave + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3)] = acc[i][j][v];
-        }
-        __syncthreads();
-        const int lrow = tid >> 2, qtr = tid & 3;
-        uint64_t L[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) L[q] = 0ull;
-        for (int c = 0; c < 64; ++c) {
-          const float x = tv[lrow * 260 + 64 * qtr + c];
-          const uint64_t key = rank_key(x, uint32_t(nt * kTBN + 64 * qtr + c));
-          if (x == x && key > L[15]) insert16(L, key);
-        }
-        // the row's four threads are adjacent lanes of one wave
-#pragma unroll
-        for (int d = 1; d < 4; d <<= 1) {
-          uint64_t brev[16];
-#pragma unroll
-          for (int q = 0; q < 16; ++q) brev[q] = __shfl_xor(L[15 - q], d, WAVE);
-          bitonic_top<16>(L, brev);
-        }
-        const int row = 64 * half + lrow;
-        const int m = m0 + row;
-        if (qtr == 0) {
-          if (m < Mact) {
-            uint64_t* o = p.cand + (int64_t(m) * p.vgroups + rg) * 16;
-            if (!first) {
-              uint64_t brev[16];
-#pragma unroll
-              for (int q = 0; q < 16; ++q) brev[q] = o[15 - q];
-              bitonic_top<16>(L, brev);
-            }
-#pragma unroll
-            for (int q = 0; q < 16; ++q) o[q] = L[q];
-            thrk[row] = L[15];
-          } else {
-            thrk[row] = ~0ull;
-          }
-        }
-      }
-      if (tid < BM) cnt[tid] = 0;
-    }
-    __syncthreads();  // LDS (slots, thrk) settled before the next tile's stages
-  }
-}
-
-// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 int tiled_block_rows(int M) {
@@ -764,15 +456,10 @@ int tiled_block_rows(int M) {
 bool gemm_tiled_ok(int weight_dtype, int M, int K) {
   return weight_dtype != 0 && M > kTiledMinRows && K % kTKT == 0;
 }
-bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k) {
-  return gemm_tiled_ok(weight_dtype, M, K) && k <= 16;
-}
-
 template <typename TW>
-static void launch_tiled_t(const TiledArgs& t, bool topk, hipStream_t s) {
+static void launch_tiled_t(const TiledArgs& t, hipStream_t s) {
   const dim3 grid(unsigned((t.tiles + 7) / 8 * 8));
-  if (topk) hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 8>), grid, dim3(256), 0, s, t);
-  else if (t.epi.kind == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8, EPI_SWIGLU>), grid, dim3(256), 0, s, t);
+  if (t.epi.kind == EPI_SWIGLU) hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8, EPI_SWIGLU>), grid, dim3(256), 0, s, t);
   else if (t.epi.kind == EPI_QKV) hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8, EPI_QKV>), grid, dim3(256), 0, s, t);
   else hipLaunchKernelGGL((gemm_tiled_kernel<TW, 8, EPI_NONE>), grid, dim3(256), 0, s, t);
 }
@@ -799,56 +486,8 @@ void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s) {
   t.nM = (a.M + tiled_block_rows(a.M) - 1) / tiled_block_rows(a.M);
   t.nN = t.epi.kind == EPI_SWIGLU ? (a.epi.F + 127) / 128 : (a.N + kTBN - 1) / kTBN;
   t.tiles = t.nM * t.nN * t.splits * t.groups;
-  if (weight_dtype == 1) launch_tiled_t<bf16_t>(t, false, s);
-  else launch_tiled_t<fp8_t>(t, false, s);
-}
-
-// Vocabulary tiles per lm_head block: the run with the shortest makespan,
-// counted in tiles on the 512 block slots (two per CU); ties go to the
-// shorter run (longer sweeps let the blocks that share a weight tile drift
-// apart, which costs more L2 hits than the cheaper later-tile filtering
-// saves).
-// DFLASH2_LMHEAD_TILES_PER_BLOCK (1..64) overrides the choice.
-int lmhead_tiles_per_block(int M, int V) {
-  const int nM = (M + tiled_block_rows(M) - 1) / tiled_block_rows(M);
-  const int nN = (V + kTBN - 1) / kTBN;
-  if (const char* env = std::getenv("DFLASH2_LMHEAD_TILES_PER_BLOCK")) {
-    const int v = std::atoi(env);
-    if (v >= 1 && v <= 64) return std::min(v, nN);
-  }
-  int best = 1;
-  long best_cost = -1;
-  for (int tpb = 1; tpb <= 32 && tpb <= nN; ++tpb) {
-    const long blocks = long(nM) * ((nN + tpb - 1) / tpb);
-    const long cost = (blocks + 511) / 512 * tpb;
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best = tpb;
-    }
-  }
-  return best;
-}
-
-int lmhead_tiled_lists(int M, int V) {
-  const int nN = (V + kTBN - 1) / kTBN;
-  const int tpb = lmhead_tiles_per_block(M, V);
-  return (nN + tpb - 1) / tpb;
-}
-
-void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
-  TiledArgs t{};
-  t.X = static_cast<const bf16_t*>(a.X); t.ldx = a.ldx;
-  t.W = a.W; t.ldw = a.ldw; t.scale = a.scale;
-  t.M = a.M; t.N = a.N; t.K = a.K; t.M_dev = a.M_dev; t.rs = a.rs;
-  t.splits = 1; t.k_split = a.K; t.groups = 1;
-  t.k = a.k; t.cand = a.cand; t.debug_logits = a.debug_logits;
-  t.nM = (a.M + tiled_block_rows(a.M) - 1) / tiled_block_rows(a.M);
-  t.nN = (a.N + kTBN - 1) / kTBN;
-  t.tpb = lmhead_tiles_per_block(a.M, a.N);
-  t.vgroups = lmhead_tiled_lists(a.M, a.N);
-  t.tiles = t.nM * t.vgroups;
-  if (weight_dtype == 1) launch_tiled_t<bf16_t>(t, true, s);
-  else launch_tiled_t<fp8_t>(t, true, s);
+  if (weight_dtype == 1) launch_tiled_t<bf16_t>(t, s);
+  else launch_tiled_t<fp8_t>(t, s);
 }
 
 }  // namespace dfl

@@ -1,0 +1,711 @@
+// lm_head + top-k for many activation rows (the batched and fp8 high-batch
+// workloads), where every lm_head row meets hundreds of activation rows and
+// the matrix cores set the pace.
+//
+// Main loop.  Block tile: 256 vocabulary rows x BM activation rows (BM = 256
+// or 128), 4 waves in a 2 x 2 layout; wave (wv, wm) owns vocabulary rows
+// [128 wv, 128 wv + 128) against activation rows [BM/2 wm, BM/2 (wm + 1)):
+// 4 x BM/64 tiles of v_mfma_f32_32x32x16_bf16 (up to 256 accumulators, one
+// wave per SIMD).  Both operands go from global memory straight into LDS
+// (global_load_lds_dwordx4: 16 bytes per lane, no register round trip), 64 k
+// per stage, two stages in flight; each stage buffer is its own LDS object,
+// so the compiler waits only for the loads of the buffer it reads.  Rows are
+// 128 bytes (activations, bf16 weights) or 64 bytes (fp8 weights) with the
+// 16-byte chunks of row r XOR-permuted by (r ^ (r >> 2)): the 32 x 32 x 16
+// operand reads (row = lane % 32, chunk by lane / 32) then hit distinct banks
+// (measured on MI355X: one LDS cycle per 256 bytes, where an unpermuted
+// layout takes eight and a (r + r / 8) permutation two).  fp8 weights read
+// 16 bytes per lane for two k steps (the k order inside each pair of steps is
+// permuted on both operands alike) and are widened to bf16 (exact) before
+// the MFMA.  Within a stage, the operand reads of step s + 1 are interleaved
+// with the MFMAs of step s; the barrier that hands over the next stage sits
+// before the last step's MFMAs, which then overlap the first reads of the
+// next stage and the loads of the stage after.
+//
+// Measured at the fp8 high-batch shape (1792 x 151936 x 5120, random data):
+// the main loop alone 2.27 ms (1.23 PF/s); with the global loads switched off
+// 1.83 ms, which is the matrix-core rate this chip sustains on random
+// operands (the same loop on all-zero operands runs at 82-86% of the nominal
+// peak, on random ones at 61%); the loads alone 1.25 ms.
+//
+// Top-k.  A block sweeps a run of consecutive 256-id vocabulary tiles for
+// its activation rows and keeps each row's 16 best keys (value desc, id asc)
+// of the run in the row's output list cand[m][run][0..16), which the merge
+// kernel reduces to the final k.  Per tile, each lane holds 64 logits of each
+// of its rows; it inserts those that beat the row's current 16th key into a
+// sorted list of 16 (after the first tile of a run few values qualify); the
+// lists of the two half-waves holding a row merge by shuffle, those of the
+// two waves through LDS, and the result merges with the run's list so far.
+// Every step is an exact ranking, so ties and -0.0 follow the key order.
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dfl {
+
+namespace {
+constexpr int kLBN = 256;  // vocabulary rows per tile
+constexpr int kLKT = 64;   // contraction depth per stage
+}  // namespace
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct LmTiledArgs {
+  const bf16_t* X; int64_t ldx;   // [M][K]
+  const void* W; int64_t ldw;     // [V][K]
+  const float* scale;             // [V] or null
+  int M, N, K;
+  const int32_t* M_dev;
+  RowScale rs;
+  uint64_t* cand;                 // [M][runs][16]
+  float* debug_logits;            // [M][N] or null
+  int nM, runs, tpb, nN;
+};
+
+// 16 bytes per lane from global memory straight into LDS at l + 16 * lane
+// (l wave-uniform).  A non-template wrapper keeps the device-only builtin out
+// of the host pass's instantiation of the kernel templates.
+__device__ __forceinline__ void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+// 16-byte chunk permutation of an LDS row
+__device__ __forceinline__ int chunk_perm(int r) { return r ^ (r >> 2); }
+
+template <typename TW, int BM>
+struct DmaTile {
+  static constexpr int SW = int(sizeof(TW));
+  static constexpr int WROW = kLKT * SW, XROW = kLKT * 2;   // LDS bytes per row and stage
+  static constexpr int WBYTES = kLBN * WROW, XBYTES = BM * XROW;
+  static constexpr int WM = BM / 2, FJ = WM / 32;
+  static constexpr int WLD = WBYTES / 4096, XLD = XBYTES / 4096;  // loads per wave and stage
+  static constexpr int WCH = WROW / 16;                        // 16-byte chunks per weight row
+
+  // acc[i][j][4 q + e] = sum over k of W[n0 + 128 wv + 32 i + 8 q + 4 h + e][k] *
+  // X[m0 + WM wm + 32 j + r][k] for lane (r, h) = (lane % 32, lane / 32) of
+  // wave (wv, wm).  Rows past N / Mact are clamped to the last row (their
+  // results are never used).  wave must be wave-uniform.
+  __device__ __forceinline__ static void run(const bf16_t* __restrict__ X, int64_t ldx, const TW* __restrict__ W,
+                                             int64_t ldw, int N, int Mact, int n0, int m0, int nk, int wave,
+                                             char* w0, char* w1, char* x0, char* x1, f32x16 (&acc)[4][FJ]) {
+    // An empty asm makes the lane index opaque, so the per-lane offsets below
+    // are recomputed on every call rather than hoisted out of the caller's
+    // tile loop and kept (spilled) across its epilogue.
+    int lane = threadIdx.x & (WAVE - 1);
+    asm volatile("" : "+v"(lane));
+    const int wv = wave & 1, wm = wave >> 1;
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) acc[i][j] = f32x16{};
+    // 64-bit tile bases; per-lane 32-bit offsets below them (a tile spans
+    // at most 256 rows of at most 2^20 elements)
+    const int wb0 = min(n0, N - 1), xb0 = min(m0, Mact - 1);
+    const char* wbase = reinterpret_cast<const char*>(W) + int64_t(wb0) * ldw * SW;
+    const char* xbase = reinterpret_cast<const char*>(X) + int64_t(xb0) * ldx * 2;
+    uint32_t woff[WLD], xoff[XLD];
+#pragma unroll
+    for (int q = 0; q < WLD; ++q) {
+      const int piece = wave * WLD + q;                   // 1 KB piece of the stage
+      const int rpp = 1024 / WROW;                        // rows per piece
+      const int row = rpp * piece + lane / WCH;
+      const int chunk = (lane % WCH) ^ (chunk_perm(row) & (WCH - 1));
+      woff[q] = uint32_t(min(n0 + row, N - 1) - wb0) * uint32_t(ldw) * SW + 16u * chunk;
+    }
+#pragma unroll
+    for (int q = 0; q < XLD; ++q) {
+      const int piece = wave * XLD + q;
+      const int row = 8 * piece + (lane >> 3);
+      const int chunk = (lane & 7) ^ (chunk_perm(row) & 7);
+      xoff[q] = uint32_t(min(m0 + row, Mact - 1) - xb0) * uint32_t(ldx) * 2 + 16u * chunk;
+    }
+    auto load_stage = [&](int kt, char* wd, char* xd) {
+#pragma unroll
+      for (int q = 0; q < WLD; ++q) lds_load16(wbase + woff[q] + uint32_t(kt * WROW), wd + 1024 * (wave * WLD + q));
+#pragma unroll
+      for (int q = 0; q < XLD; ++q) lds_load16(xbase + xoff[q] + uint32_t(kt * XROW), xd + 1024 * (wave * XLD + q));
+    };
+    // operand read offsets: weights per (i, step) (bf16) or (i, pair of
+    // steps) (fp8); activations per (j, step)
+    int wrd[4][4], xrd[FJ][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 128 * wv + 32 * i + r;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = SW == 2 ? 2 * s + h : 2 * (s >> 1) + h;
+        wrd[i][s] = row * WROW + 16 * (c ^ (chunk_perm(row) & (WCH - 1)));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int row = WM * wm + 32 * j + r;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // fp8: step s, half h covers k = 32 (s / 2) + 16 h + 8 (s % 2) + 0..7
+        const int c = SW == 2 ? 2 * s + h : 4 * (s >> 1) + 2 * h + (s & 1);
+        xrd[j][s] = row * XROW + 16 * (c ^ (chunk_perm(row) & 7));
+      }
+    }
+    u32x4 wr[2][4];     // bf16: by step parity; fp8: raw bytes of a pair of steps, by pair parity
+    bf16x8 xr[2][FJ];   // by step parity
+    auto prefetch = [&](int s, const char* wl, const char* xl) {
+      if (SW == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wr[s & 1][i] = *reinterpret_cast<const u32x4*>(wl + wrd[i][s]);
+      } else if ((s & 1) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wr[(s >> 1) & 1][i] = *reinterpret_cast<const u32x4*>(wl + wrd[i][s]);
+      }
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) xr[s & 1][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + xrd[j][s]));
+    };
+    auto mfmas = [&](int s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Frag8Bf16 a;
+        if (SW == 2) {
+          a.v = __builtin_bit_cast(bf16x8, wr[s & 1][i]);
+        } else {
+          const u32x4 w = wr[(s >> 1) & 1][i];
+          fp8x8_to_frag(a, (s & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+        }
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, xr[s & 1][j], acc[i][j], 0, 0, 0);
+      }
+    };
+    auto nreads = [&](int s) { return FJ + ((SW == 2 || (s & 1) == 0) ? 4 : 0); };
+    // one MFMA, then one DS read (while reads remain), ...
+    auto interleave = [&](int nrd, int nvm) {
+#pragma unroll
+      for (int q = 0; q < 4 * FJ; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (q < nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+    // One stage on (wl, xl), whose step 0 operands are already requested;
+    // the next stage is in (wn, xn); after the barrier the loads of stage
+    // kt_load go into (wl, xl), which no wave reads any more.
+    auto stage = [&](char* wl, char* xl, const char* wn, const char* xn, int kt_load) {
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        prefetch(s + 1, wl, xl);
+        mfmas(s);
+        interleave(nreads(s + 1), 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next stage, and its reads of this one
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(kt_load, wl, xl);
+      prefetch(0, wn, xn);
+      mfmas(3);
+      interleave(nreads(0), WLD + XLD);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    load_stage(0, w0, x0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    load_stage(min(1, nk - 1), w1, x1);
+    prefetch(0, w0, x0);
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      stage(w0, x0, w1, x1, min(kt + 2, nk - 1));
+      stage(w1, x1, w0, x0, min(kt + 3, nk - 1));
+    }
+    if (kt < nk) stage(w0, x0, w1, x1, nk - 1);
+    __builtin_amdgcn_s_waitcnt(0);   // the last (repeated) loads have landed before LDS is reused
+  }
+};
+
+// L (16 keys, largest first) <- the 16 largest of L and x.
+__device__ __forceinline__ void insert_key(uint64_t (&L)[16], uint64_t x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool c = x > L[i];
+    const uint64_t t = L[i];
+    L[i] = c ? x : t;
+    x = c ? t : x;
+  }
+}
+
+// a (16 keys) sorted descending in place (bitonic network).
+__device__ __forceinline__ void sort16_keys_desc(uint64_t (&a)[16]) {
+#pragma unroll
+  for (int size = 2; size <= 16; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ stride;
+        if (l > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t x = a[i], y = a[l];
+          const bool sw = desc ? (y > x) : (x > y);
+          a[i] = sw ? y : x;
+          a[l] = sw ? x : y;
+        }
+      }
+}
+
+// a (16 floats) sorted descending in place.
+__device__ __forceinline__ void sort16_desc(float (&a)[16]) {
+#pragma unroll
+  for (int size = 2; size <= 16; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ stride;
+        if (l > i) {
+          const bool desc = (i & size) == 0;
+          const float hi = fmaxf(a[i], a[l]), lo = fminf(a[i], a[l]);
+          a[i] = desc ? hi : lo;
+          a[l] = desc ? lo : hi;
+        }
+      }
+}
+
+// Per tile and row, only values that can still enter the row's 16 best are
+// looked at:
+//  * first tile of a run: each lane keeps the largest and second largest of
+//    each group of 16 of its values; the 16th largest of a row's 32 such
+//    values is a bound T with at least 16 of the row's values >= T, so no
+//    value below T can be among the row's best 16;
+//  * later tiles: the row's current 16th key.
+// Passing values (about 18 of a row's 256 on a first tile, rarely any later)
+// are staged in LDS by the lanes of rows that have some and inserted into
+// the lane's sorted list of 16; rows whose lanes found nothing keep their
+// list untouched.
+template <typename TW, int BM>
+__global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
+  typedef DmaTile<TW, BM> T;
+  constexpr int FJ = T::FJ, WM = T::WM;
+  __shared__ __attribute__((aligned(1024))) char w0[T::WBYTES];
+  __shared__ __attribute__((aligned(1024))) char w1[T::WBYTES];
+  __shared__ __attribute__((aligned(1024))) char x0[T::XBYTES];
+  __shared__ __attribute__((aligned(1024))) char x1[T::XBYTES];
+  __shared__ float inv[BM];
+  __shared__ float thr[BM];       // first tile of a run: the bound T
+  __shared__ uint64_t thrk[BM];   // the row's current 16th key of the run (0: fewer than 16 so far)
+  __shared__ f32x4 vscale4[kLBN / 4];  // the tile's per-vocabulary-row scales (1 without them)
+  __shared__ int cnt[BM];         // keys appended to the row's slots in this tile
+  // block -> (row tile, run of vocabulary tiles); blocks of one run are adjacent
+  const int per = gridDim.x >> 3;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= p.nM * p.runs) return;
+  const int mt = t % p.nM, rg = t / p.nM;
+  const int nt0 = rg * p.tpb, nt1 = min(p.nN, nt0 + p.tpb);
+  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
+  const int m0 = mt * BM;
+  if (m0 >= Mact || nt0 >= nt1) return;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave & 1, wm = wave >> 1;
+  const int r = lane & 31, h = lane >> 5;
+  for (int q = tid; q < BM; q += blockDim.x) {
+    float v = 1.f;
+    const int m = m0 + q;
+    if (p.rs.sumsq && m < Mact) {
+      float s = 0.f;
+      for (int c = 0; c < p.rs.blocks; ++c) s += p.rs.sumsq[int64_t(m) * p.rs.blocks + c];
+      v = 1.0f / sqrtf(s * p.rs.inv_width + p.rs.eps);
+    }
+    inv[q] = v;
+    thrk[q] = 0ull;
+    cnt[q] = 0;
+  }
+  // (inv and thrk are read after the main loop's barriers)
+  const TW* W = static_cast<const TW*>(p.W);
+  const int nk = p.K / kLKT;
+  for (int nt = nt0; nt < nt1; ++nt) {
+    const int n0 = nt * kLBN;
+    const bool fresh = nt == nt0;
+    // (the previous tile's epilogue ended with a barrier; vscale is read
+    // after the main loop's barriers)
+    if (tid < kLBN / 4) {
+      f32x4 sv = {1.f, 1.f, 1.f, 1.f};
+      const int n = n0 + 4 * tid;
+      if (sizeof(TW) == 1 && p.scale) {
+        if (n + 3 < p.N) {
+          sv = *reinterpret_cast<const f32x4*>(p.scale + n);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[e] = p.scale[min(n + e, p.N - 1)];
+        }
+      }
+      vscale4[tid] = sv;
+    }
+    f32x16 acc[4][FJ];
+    T::run(p.X, p.ldx, W, p.ldw, p.N, Mact, n0, m0, nk, wave, w0, w1, x0, x1, acc);
+    // lane (r, h) of wave (wv, wm): value 4 q + e of acc[i][j] is vocabulary id
+    // n0 + lb + 32 i + 8 q + e, lb = 128 wv + 4 h, of local row WM wm + 32 j + r.
+    // Per-lane values are recomputed per tile (see DmaTile::run).
+    int lb = 128 * wv + 4 * h;
+    asm volatile("" : "+v"(lb));
+    const int nvalid = p.N - n0 - lb;   // ids at offsets < nvalid exist
+    __syncthreads();  // every wave's loads have landed and the stage buffers are free
+    // the run's list so far of row tid (requested now, used after the
+    // appends below, so the load latency is hidden)
+    uint64_t G[16];
+    {
+      const int m = m0 + tid;
+      const bool cont = !fresh && tid < BM && m < Mact;
+      const uint64_t* o = p.cand + (int64_t(min(m, p.M - 1)) * p.runs + rg) * 16;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) G[q] = cont ? o[q] : 0ull;
+    }
+
+    // Logits of the lane's 32 values of row j, half hf (vocabulary offsets
+    // lb + 64 hf + voff(k), k < 32), copied out of the accumulators by a
+    // switch on (j, hf), so that a single copy of the code below, in loops
+    // that are not unrolled, serves every row: unrolled per row it would not
+    // fit the instruction cache.
+    auto voff = [](int k) { return 32 * (k >> 4) + 8 * ((k & 15) >> 2) + (k & 3); };
+    auto logits_half = [&](int jh, float (&x)[32]) {
+      const int j = jh >> 1, hf = jh & 1;
+      const float iv = inv[WM * wm + 32 * j + r];
+      float sv[32];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const f32x4 v4 = vscale4[(lb + 64 * hf + voff(4 * g)) >> 2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * g + e] = v4[e];
+      }
+      auto take = [&](auto J, auto HF) {
+        constexpr int jj = decltype(J)::value, hh = decltype(HF)::value;
+        if constexpr (jj < FJ) {
+#pragma unroll
+          for (int k = 0; k < 32; ++k) x[k] = acc[2 * hh + (k >> 4)][jj][k & 15];
+        }
+      };
+      switch (jh) {
+        case 0: take(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}); break;
+        case 1: take(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}); break;
+        case 2: take(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}); break;
+        case 3: take(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); break;
+        case 4: take(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{}); break;
+        case 5: take(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}); break;
+        case 6: take(std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{}); break;
+        default: take(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{}); break;
+      }
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        float y = x[k];
+        y *= sv[k];
+        y *= iv;
+        x[k] = y + 0.0f;
+      }
+    };
+    static_assert(FJ <= 4, "at most four row blocks per wave");
+    // bit k: value x[k] can enter the row's list (ids past the vocabulary
+    // never do).  Branch-free: first tile of a run, x >= T; later, the key
+    // beats the row's 16th key tk (any number while the list is not full).
+    auto pass_mask = [&](const float (&x)[32], int base, int hf, float tf, float tv, uint32_t tlo, bool tk0) {
+      uint32_t mask = 0u;
+      if (fresh) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+          mask |= (uint32_t(x[k] >= tf) & uint32_t(64 * hf + voff(k) < nvalid)) << k;
+      } else {
+        const uint32_t any = uint32_t(tk0);
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const float y = x[k];
+          const uint32_t beats = uint32_t(y > tv) |
+                                 (uint32_t(y == tv) & uint32_t(0xFFFFFFFFu - uint32_t(n0 + base + voff(k)) > tlo));
+          const uint32_t ok = (any & uint32_t(y == y)) | beats;
+          mask |= (ok & uint32_t(64 * hf + voff(k) < nvalid)) << k;
+        }
+      }
+      return mask;
+    };
+
+    // 1. first tile of a run: the bound T of each row
+    if (fresh) {
+      float* ab = reinterpret_cast<float*>(x0);  // [32 slots][BM rows]
+#pragma nounroll
+      for (int jh = 0; jh < 2 * FJ; ++jh) {
+        float x[32];
+        logits_half(jh, x);
+        const int lm = WM * wm + 32 * (jh >> 1) + r;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          float a = -INFINITY, b = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float y = 64 * (jh & 1) + voff(16 * ii + v) < nvalid ? x[16 * ii + v] : -INFINITY;
+            b = fmaxf(b, fminf(a, y));
+            a = fmaxf(a, y);
+          }
+          const int slot = ((wv * 2 + h) * 4 + 2 * (jh & 1) + ii) * 2;
+          ab[slot * BM + lm] = a;
+          ab[(slot + 1) * BM + lm] = b;
+        }
+      }
+      __syncthreads();
+      if (tid < BM) {
+        // the 16 largest of the union of the sorted maxima A and second
+        // maxima B are max(A[q], B[15 - q]); T is their minimum
+        float A[16], B[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          A[q] = ab[(2 * q) * BM + tid];
+          B[q] = ab[(2 * q + 1) * BM + tid];
+        }
+        sort16_desc(A);
+        sort16_desc(B);
+        float Tb = INFINITY;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) Tb = fminf(Tb, fmaxf(A[q], B[15 - q]));
+        thr[tid] = Tb;
+      }
+      __syncthreads();
+    }
+
+    // 2. common path.  The debug copy first (only when asked for); then every
+    // lane compares each of its values with the row's bound (first tile: T;
+    // later: the value of the row's 16th key, ties passing, since the id
+    // order is settled by the exact key comparison of the insertion below;
+    // any value while the list is not full) and appends the keys of those
+    // that pass to the row's slots in LDS (one atomic per lane and row).
+    // Slots of rows [0, WM) are in x0, of rows [WM, BM) in x1 (free now: the
+    // bounds above were read before the last barrier).
+    constexpr int NSLOT = 32;
+    static_assert(WM * NSLOT * 8 <= T::XBYTES, "slots fit an activation stage buffer");
+    float* stg = reinterpret_cast<float*>(wave < 2 ? w0 : w1) + (wave & 1) * 32 * WAVE;  // [32][64] per wave
+    static_assert(2 * 32 * WAVE * 4 <= T::WBYTES, "staging fits a weight stage buffer");
+    auto slots_of = [&](int lm) {
+      return reinterpret_cast<uint64_t*>(lm < WM ? x0 : x1) + (lm % WM) * NSLOT;
+    };
+    if (p.debug_logits) {
+#pragma nounroll
+      for (int jh = 0; jh < 2 * FJ; ++jh) {
+        float x[32];
+        logits_half(jh, x);
+        const int m = m0 + WM * wm + 32 * (jh >> 1) + r;
+        const int hf = jh & 1;
+        if (m < Mact) {
+          float* row = p.debug_logits + int64_t(m) * p.N + n0 + lb + 64 * hf;
+#pragma unroll
+          for (int g = 0; g < 8; ++g) {
+            const int off = voff(4 * g);
+            float* dst = row + off;
+            if (64 * hf + off + 3 < nvalid && (p.N & 3) == 0) {
+              *reinterpret_cast<f32x4*>(dst) = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (64 * hf + off + e < nvalid) dst[e] = x[4 * g + e];
+            }
+          }
+        }
+      }
+    }
+#pragma nounroll
+    for (int jh = 0; jh < 2 * FJ; ++jh) {
+      const int lm = WM * wm + 32 * (jh >> 1) + r;
+      const int base = lb + 64 * (jh & 1);   // vocabulary offset of x[0] in the tile
+      const uint64_t tk = thrk[lm];
+      const float te = fresh ? thr[lm] : (tk == 0ull ? -__FLT_MAX__ : key_val(tk));
+      float x[32];
+      logits_half(jh, x);
+      uint32_t mk = 0u;
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        mk |= (uint32_t(x[k] >= te) & uint32_t(64 * (jh & 1) + voff(k) < nvalid)) << k;
+      if (mk != 0u) {
+        // stage the 32 values (lane-major, wave-private) and visit the set bits
+#pragma unroll
+        for (int k = 0; k < 32; ++k) stg[k * WAVE + lane] = x[k];
+        uint64_t* sl = slots_of(lm);
+        int pos = atomicAdd(&cnt[lm], __builtin_popcount(mk));
+        while (mk != 0u) {
+          const int k = __builtin_ctz(mk);
+          mk &= mk - 1u;
+          if (pos < NSLOT) sl[pos] = rank_key(stg[k * WAVE + lane], uint32_t(n0 + base + voff(k)));
+          ++pos;
+        }
+      }
+    }
+    if (!__syncthreads_or(tid < BM && cnt[tid] > NSLOT)) {
+      if (tid < BM) {
+        const int lm = tid, m = m0 + lm;
+        const int c = cnt[lm];
+        if (m < Mact && (c > 0 || fresh)) {
+          uint64_t* o = p.cand + (int64_t(m) * p.runs + rg) * 16;
+          // the new keys, 16 at a time: sorted, then merged with the list
+          // (a sorting network and a half-cleaner cascade: short dependency
+          // chains, unlike one insertion per key)
+          const uint64_t* sl = slots_of(lm);
+          for (int q0 = 0; q0 < c; q0 += 16) {
+            uint64_t Nk[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) Nk[q] = q0 + q < c ? sl[q0 + q] : 0ull;
+            sort16_keys_desc(Nk);
+            uint64_t rev[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) rev[q] = Nk[15 - q];
+            bitonic_top<16>(G, rev);
+          }
+#pragma unroll
+          for (int q = 0; q < 16; ++q) o[q] = G[q];
+          thrk[lm] = G[15];
+        } else if (m >= Mact) {
+          thrk[lm] = ~0ull;   // rows past the last one are never output
+        }
+        cnt[lm] = 0;
+      }
+      __syncthreads();  // lists and thresholds settled before the next tile's loads reuse LDS
+      continue;
+    }
+
+    // 3. rare (heavy ties): some row has more passing values than slots.
+    // Exact per-lane lists instead: each lane inserts its passing values into
+    // a sorted list of 16; the lists of the two half-waves merge by shuffle
+    // and one copy per wave goes to LDS ([0, WM): wave wv = 1, [WM, 2 WM):
+    // wave wv = 0), where one thread per row merges them into the run's list.
+    uint64_t* lists = reinterpret_cast<uint64_t*>(wm ? x1 : x0);
+#pragma nounroll
+    for (int j = 0; j < FJ; ++j) {
+      const int lm = WM * wm + 32 * j + r;
+      const int m = m0 + lm;
+      const uint64_t tk = thrk[lm];
+      const float tf = fresh ? thr[lm] : 0.f;
+      const float tv = key_val(tk);
+      const uint32_t tlo = uint32_t(tk);
+      uint64_t L[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) L[q] = 0ull;
+#pragma nounroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float x[32];
+        logits_half(2 * j + hf, x);
+        const int base = lb + 64 * hf;   // vocabulary offset of x[0] in the tile
+        uint32_t mask = pass_mask(x, base, hf, tf, tv, tlo, tk == 0ull);
+        if (__builtin_amdgcn_ballot_w64(mask != 0u) != 0ull) {
+          // stage the 32 values (lane-major) and visit the set bits
+#pragma unroll
+          for (int k = 0; k < 32; ++k) stg[k * WAVE + lane] = x[k];
+          while (mask != 0u) {
+            const int k = __builtin_ctz(mask);
+            mask &= mask - 1u;
+            const uint64_t key = rank_key(stg[k * WAVE + lane], uint32_t(n0 + base + voff(k)));
+            if (key > L[15]) insert_key(L, key);
+          }
+        }
+      }
+      uint64_t brev[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) brev[q] = __shfl_xor(L[15 - q], 32, WAVE);
+      bitonic_top<16>(L, brev);
+      if (h == 0) {
+        uint64_t* dst = lists + ((wv ? 0 : WM) + 32 * j + r) * 16;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) dst[q] = L[q];
+      }
+    }
+    __syncthreads();
+    // each row's new candidates into the run's list (one thread per row;
+    // rows with none keep their list)
+    for (int lm = tid; lm < BM; lm += blockDim.x) {
+      const int m = m0 + lm;
+      const int half = lm / WM, lr = lm % WM;
+      const uint64_t* ls = reinterpret_cast<const uint64_t*>(half ? x1 : x0);
+      const bool any = ls[(WM + lr) * 16] != 0ull || ls[lr * 16] != 0ull;
+      if (m < Mact && (any || fresh)) {
+        uint64_t* o = p.cand + (int64_t(m) * p.runs + rg) * 16;
+        uint64_t A[16], B[16], G[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) G[q] = fresh ? 0ull : o[15 - q];   // the run's list so far, reversed
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          A[q] = ls[(WM + lr) * 16 + q];
+          B[q] = ls[lr * 16 + 15 - q];
+        }
+        bitonic_top<16>(A, B);
+        bitonic_top<16>(A, G);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) o[q] = A[q];
+        thrk[lm] = A[15];
+      } else if (m >= Mact) {
+        thrk[lm] = ~0ull;   // rows past the last one are never output
+      }
+      cnt[lm] = 0;
+    }
+    __syncthreads();  // lists and thresholds settled before the next tile's loads reuse LDS
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+namespace {
+struct LmPlan {
+  int bm, nM, nN, runs, tpb;
+};
+
+// Row tile (256 or 128 rows) and vocabulary runs: one block per CU (256
+// resident blocks), each sweeping tpb tiles; the choice minimises tpb times
+// the relative cost of a tile (a 128-row tile measured 0.6 of a 256-row one).
+// DFLASH2_LMHEAD_TILES_PER_BLOCK (1..64) overrides tpb.
+LmPlan lm_plan(int M, int V) {
+  LmPlan best{};
+  double best_cost = 1e300;
+  int force = 0;
+  if (const char* env = std::getenv("DFLASH2_LMHEAD_TILES_PER_BLOCK")) {
+    const int v = std::atoi(env);
+    if (v >= 1 && v <= 64) force = v;
+  }
+  for (int bm : {256, 128}) {
+    LmPlan pl;
+    pl.bm = bm;
+    pl.nM = (M + bm - 1) / bm;
+    pl.nN = (V + kLBN - 1) / kLBN;
+    const int runs_max = std::max(1, std::min(pl.nN, 256 / std::max(1, pl.nM)));
+    pl.tpb = force ? std::min(force, pl.nN) : (pl.nN + runs_max - 1) / runs_max;
+    pl.runs = (pl.nN + pl.tpb - 1) / pl.tpb;
+    const double waves = double((int64_t(pl.nM) * pl.runs + 255) / 256);
+    const double cost = waves * pl.tpb * (bm == 256 ? 1.0 : 0.6);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = pl;
+    }
+  }
+  return best;
+}
+}  // namespace
+
+bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k) {
+  return weight_dtype != 0 && M > kTiledMinRows && K % kLKT == 0 && k <= 16;
+}
+
+int lmhead_tiled_lists(int M, int V) { return lm_plan(M, V).runs; }
+
+template <typename TW>
+static void launch_lm_t(const LmTiledArgs& a, int bm, hipStream_t s) {
+  const int blocks = a.nM * a.runs;
+  const dim3 grid(unsigned((blocks + 7) / 8 * 8));
+  if (bm == 256) hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 256>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 128>), grid, dim3(256), 0, s, a);
+}
+
+void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
+  const LmPlan pl = lm_plan(a.M, a.N);
+  LmTiledArgs t{};
+  t.X = static_cast<const bf16_t*>(a.X); t.ldx = a.ldx;
+  t.W = a.W; t.ldw = a.ldw; t.scale = a.scale;
+  t.M = a.M; t.N = a.N; t.K = a.K; t.M_dev = a.M_dev; t.rs = a.rs;
+  t.cand = a.cand; t.debug_logits = a.debug_logits;
+  t.nM = pl.nM; t.runs = pl.runs; t.tpb = pl.tpb; t.nN = pl.nN;
+  if (weight_dtype == 1) launch_lm_t<bf16_t>(t, pl.bm, s);
+  else launch_lm_t<fp8_t>(t, pl.bm, s);
+}
+
+}  // namespace dfl
