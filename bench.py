@@ -41,7 +41,7 @@ def log(msg):
 # helpers and argument structs).
 KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "gemm_tiled.hip", "common.h", "kernels.h"],
-    "lmhead_topk": ["gemm.hip", "gemm_tiled.hip", "common.h", "kernels.h"],
+    "lmhead_topk": ["gemm.hip", "lmhead_tiled.hip", "common.h", "kernels.h"],
     "attention": ["attention.hip", "common.h", "kernels.h"],
 }
 
@@ -92,6 +92,58 @@ def attention_kv_bytes(w, ctx_lens) -> int:
         lo = max(0, int(L) - w.sliding_window) if w.sliding_window > 0 else 0
         rows += int(L) - lo + w.block_size
     return rows * w.num_kv_heads * w.head_dim * 2 * ab
+
+
+def measure_peaks():
+    """The rates this chip sustains (library kernels dflash2_peak_mfma and
+    dflash2_peak_read): bf16 MFMA on register-resident random and all-zero
+    operands, and a non-temporal streaming read of 2 GiB."""
+    import torch
+    from block_speculative_decoding_dflash2_amd import _lib as L
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    blocks, iters = 1024, 4000
+    buf = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    for zero, key in ((0, "mfma_bf16_random_tflops"), (1, "mfma_bf16_zero_tflops")):
+        L.dflash2_peak_mfma(stream, blocks, 50, zero, buf.data_ptr())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = 0.0
+        for _ in range(3):
+            e0.record()
+            L.dflash2_peak_mfma(stream, blocks, iters, zero, buf.data_ptr())
+            e1.record()
+            torch.cuda.synchronize()
+            flops = blocks * 4 * iters * 16 * 32768
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        out[key] = round(best, 1)
+    nbytes = 2 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    rblocks = 4096
+    rout = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
+    L.dflash2_peak_read(stream, src.data_ptr(), nbytes, rblocks, rout.data_ptr())
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(5):
+        e0.record()
+        L.dflash2_peak_read(stream, src.data_ptr(), nbytes, rblocks, rout.data_ptr())
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    out["hbm_read_gbs"] = round(best, 1)
+    del src, rout, buf
+    torch.cuda.empty_cache()
+    log(f"measured peaks: {out}")
+    return out
+
+
+def add_measured_fraction(roofline, peaks):
+    if not roofline or not peaks:
+        return
+    ref = peaks["hbm_read_gbs"] if roofline["bound"] == "hbm" else peaks["mfma_bf16_random_tflops"]
+    roofline["peak_measured"] = ref
+    roofline["frac_of_measured"] = round(roofline["achieved"] / ref, 4)
 
 
 def run_workload(name, args, primary: bool):
@@ -353,6 +405,7 @@ def main():
                     help="run the workload with dynamic grouped convolution (channels per group)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA / HBM read ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -361,7 +414,9 @@ def main():
               f"--gpus {args.gpus} is not supported (run one process per GPU).", file=sys.stderr)
         sys.exit(2)
 
+    peaks = None if args.no_peaks else measure_peaks()
     main_r = run_workload(args.workload, args, primary=True)
+    add_measured_fraction(main_r["roofline"], peaks)
     w = main_r["w"]
     rec = record(main_r, args)
     out = {
@@ -384,7 +439,10 @@ def main():
         out["extra_workloads"] = []
         for name in extras:
             r = run_workload(name, args, primary=False)
+            add_measured_fraction(r["roofline"], peaks)
             out["extra_workloads"].append(record(r, args))
+    if peaks:
+        out["measured_peaks"] = peaks
     print(json.dumps(out), flush=True)
 
 

@@ -92,6 +92,8 @@ def _load():
         "dflash2_draft_losses_workspace_size": ([c_int32, c_int32, c_int32, POINTER(c_size_t)], c_int32),
         "dflash2_draft_losses": ([vp, vp, c_int32, i32p, i32p, f32p, i32p, f32p, c_float, c_float, f32p, f32p,
                                   f32p, vp, c_size_t], c_int32),
+        "dflash2_peak_mfma": ([vp, c_int32, c_int32, c_int32, f32p], c_int32),
+        "dflash2_peak_read": ([vp, vp, c_size_t, c_int32, vp], c_int32),
         "dflash2_trace_attach": ([POINTER(dflash2_trace_entry), c_int32], c_int32),
         "dflash2_trace_detach": ([], c_int32),
         "dflash2_last_error": ([], ctypes.c_char_p),
@@ -109,7 +111,16 @@ EXPORTED = ("dflash2_create", "dflash2_destroy", "dflash2_workspace_size", "dfla
             "dflash2_verify_accept", "dflash2_verify_accept_noalloc", "dflash2_verify_sample_workspace_size",
             "dflash2_verify_sample",
             "dflash2_draft_losses_workspace_size", "dflash2_draft_losses",
-            "dflash2_trace_attach", "dflash2_trace_detach", "dflash2_last_error")
+            "dflash2_trace_attach", "dflash2_trace_detach", "dflash2_last_error", "dflash2_peak_mfma",
+            "dflash2_peak_read")
+
+
+def dflash2_peak_mfma(stream, blocks, iters, zero_operands, out) -> None:
+    _check(lib.dflash2_peak_mfma(stream, blocks, iters, zero_operands, out))
+
+
+def dflash2_peak_read(stream, src, nbytes, blocks, out) -> None:
+    _check(lib.dflash2_peak_read(stream, src, nbytes, blocks, out))
 
 
 def dflash2_trace_attach(entries, capacity: int) -> None:

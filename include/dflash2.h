@@ -433,6 +433,27 @@ int32_t dflash2_trace_detach(void);
 /* Description of the last error on the calling thread ("" if none). */
 const char* dflash2_last_error(void);
 
+/* Measured ceilings (benchmark utilities, not part of the step).  They give
+ * the rates this chip sustains, reported beside the nominal MI355X peaks
+ * (dense bf16 MFMA 2.5 PFLOP/s, HBM3E 8 TB/s).
+ *
+ * dflash2_peak_mfma: `blocks` blocks of 4 waves (one per SIMD), each wave
+ * running `iters` rounds of 16 independent v_mfma_f32_32x32x16_bf16 on
+ * operands held in registers: 16 * 32768 flops per wave and round.  With
+ * zero_operands != 0 every operand is 0.0, otherwise a per-lane pseudo-random
+ * bf16 value in +-[0.5, 2).  out [device] float [blocks * 4] receives one sum
+ * per wave.  Time the call with events on `stream`.
+ *
+ * dflash2_peak_read: `blocks` blocks of 256 threads read `bytes` (multiple
+ * of 16; src 16-byte aligned) of src [device] once, 16 bytes per lane with
+ * non-temporal loads; out [device] uint32 [blocks * 256] receives per-thread
+ * checksums.
+ * Errors: DFLASH2_ERR_INVALID_ARG for bad sizes or pointers. */
+dflash2_status dflash2_peak_mfma(hipStream_t stream, int32_t blocks, int32_t iters, int32_t zero_operands,
+                                 float* out);
+dflash2_status dflash2_peak_read(hipStream_t stream, const void* src, size_t bytes, int32_t blocks,
+                                 uint32_t* out);
+
 #ifdef __cplusplus
 }
 #endif
