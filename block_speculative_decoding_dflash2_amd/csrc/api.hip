@@ -68,6 +68,14 @@ constexpr int kTargetBlocks = 512;  // 2 blocks of 4 waves per CU on 256 CUs
 constexpr int kStreamBlockOverhead = 256;  // fixed cost of one weight-streaming block, in k
 constexpr int64_t kStreamMaxRowBytes = 3072;  // longest per-block stream of one weight row
 constexpr size_t kAlign = 256;
+// Row bounds shared by every entry point: block_size <= 4096 (the greedy
+// verifier keeps a block's argmaxes in LDS) and batch * block_size <= 2^30
+// rows (row indices are 32-bit and rows are grid x-blocks).
+constexpr int32_t kMaxBlockSize = 4096;
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+bool rows_ok(int32_t batch, int32_t block_size) {
+  return batch >= 1 && block_size >= 2 && block_size <= kMaxBlockSize && int64_t(batch) * block_size <= kMaxRows;
+}
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -283,7 +291,9 @@ dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weight
     return fail(DFLASH2_ERR_INVALID_ARG, "create: sizes must be positive");
   if (c.weight_dtype < DFLASH2_FP32 || c.weight_dtype > DFLASH2_FP8_E4M3)
     return fail(DFLASH2_ERR_INVALID_ARG, "create: unknown weight_dtype %d", c.weight_dtype);
-  if (c.block_size < 2) return fail(DFLASH2_ERR_SHAPE, "create: block_size %d < 2", c.block_size);
+  if (!rows_ok(c.max_batch, c.block_size))
+    return fail(DFLASH2_ERR_SHAPE, "create: block_size %d outside 2..4096 or max_batch * block_size > 2^30",
+                c.block_size);
   if (c.num_q_heads % c.num_kv_heads)
     return fail(DFLASH2_ERR_SHAPE, "create: num_q_heads %d not a multiple of num_kv_heads %d",
                 c.num_q_heads, c.num_kv_heads);
@@ -696,7 +706,7 @@ extern "C" {
 dflash2_status dflash2_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
                                              size_t* bytes) {
   if (!bytes) return fail(DFLASH2_ERR_INVALID_ARG, "verify_workspace_size: null argument");
-  if (batch < 1 || block_size < 2 || vocab < 1)
+  if (!rows_ok(batch, block_size) || vocab < 1)
     return fail(DFLASH2_ERR_SHAPE, "verify_workspace_size: bad sizes");
   *bytes = plan_verify(batch, block_size, vocab).bytes;
   return ok();
@@ -740,7 +750,7 @@ dflash2_status dflash2_verify_accept(hipStream_t stream, int32_t batch, int32_t 
                                      const float* target_logits, int32_t* accepted,
                                      int32_t* bonus, int32_t* target_argmax, void* workspace,
                                      size_t workspace_bytes) {
-  if (batch < 1 || block_size < 2 || vocab < 1)
+  if (!rows_ok(batch, block_size) || vocab < 1)
     return fail(DFLASH2_ERR_SHAPE, "verify_accept: bad sizes (batch %d, block_size %d, vocab %d)",
                 batch, block_size, vocab);
   if (!draft_tokens || !target_logits || !accepted || !bonus)
@@ -802,7 +812,7 @@ dflash2_status dflash2_verify_accept_noalloc(hipStream_t stream, int32_t batch, 
                                              int32_t vocab, const int32_t* draft_tokens,
                                              const float* target_logits, int32_t* accepted,
                                              int32_t* bonus, int32_t* target_argmax) {
-  if (batch < 1 || block_size < 2 || vocab < 1)
+  if (!rows_ok(batch, block_size) || vocab < 1)
     return fail(DFLASH2_ERR_SHAPE, "verify_accept_noalloc: bad sizes (batch %d, block_size %d, vocab %d)",
                 batch, block_size, vocab);
   if (!draft_tokens || !target_logits || !accepted || !bonus)
@@ -824,7 +834,7 @@ dflash2_status dflash2_verify_accept_noalloc(hipStream_t stream, int32_t batch, 
 dflash2_status dflash2_verify_sample_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
                                                     size_t* bytes) {
   if (!bytes) return fail(DFLASH2_ERR_INVALID_ARG, "verify_sample_workspace_size: null argument");
-  if (batch < 1 || block_size < 2 || vocab < 1)
+  if (!rows_ok(batch, block_size) || vocab < 1)
     return fail(DFLASH2_ERR_SHAPE, "verify_sample_workspace_size: bad sizes");
   *bytes = std::max(plan_verify(batch, block_size, vocab).bytes, sample_ws_bytes(batch, block_size));
   return ok();
@@ -835,7 +845,7 @@ dflash2_status dflash2_verify_sample(hipStream_t stream, int32_t batch, int32_t 
                                      const float* target_logits, const float* uniforms, float temperature,
                                      int32_t top_k, float top_p, int32_t* accepted, int32_t* bonus,
                                      float* draft_prob, void* workspace, size_t workspace_bytes) {
-  if (batch < 1 || block_size < 2 || vocab < 1)
+  if (!rows_ok(batch, block_size) || vocab < 1)
     return fail(DFLASH2_ERR_SHAPE, "verify_sample: bad sizes (batch %d, block_size %d, vocab %d)",
                 batch, block_size, vocab);
   if (!draft_tokens || !target_logits || !accepted || !bonus)
@@ -889,7 +899,7 @@ dflash2_status dflash2_verify_sample(hipStream_t stream, int32_t batch, int32_t 
 dflash2_status dflash2_draft_losses_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
                                                   size_t* bytes) {
   if (!bytes) return fail(DFLASH2_ERR_INVALID_ARG, "draft_losses_workspace_size: null argument");
-  if (batch < 1 || block_size < 2 || vocab < 1)
+  if (!rows_ok(batch, block_size) || vocab < 1)
     return fail(DFLASH2_ERR_SHAPE, "draft_losses_workspace_size: bad sizes");
   const VerifyPlan lp = plan_verify(batch, block_size - 1, vocab);
   *bytes = align_up(size_t(batch) * (block_size - 1) * lp.nchunks * 8) + align_up(size_t(batch) * 6 * 8);

@@ -3,7 +3,7 @@
 // 1..bs-1, the selector cross-entropy over each position's top-k candidates
 // scored against the ground-truth predecessor, and candidate_recall.
 //
-//   loss_rows_kernel  grid (chunks, B*(bs-1)): per vocabulary chunk of a row,
+//   loss_rows_kernel  grid (B*(bs-1), chunks): per vocabulary chunk of a row,
 //                     the running maximum and sum of exp of the transformed
 //                     logits (one pass, online rescaling);
 //   loss_seq_kernel   one block per sequence: merges a row's chunks in order
@@ -55,10 +55,10 @@ __device__ __forceinline__ void wave_lse(float& m, float& s) {
 
 }  // namespace
 
-// grid = (nchunks, rows), block = 256.
+// grid = (rows, nchunks), block = 256.
 __global__ __launch_bounds__(256) void loss_rows_kernel(LossArgs p) {
   __shared__ float sm[8], ss[8];
-  const int c = blockIdx.x, row = blockIdx.y;
+  const int row = blockIdx.x, c = blockIdx.y;
   const int v0 = c * p.chunk, v1 = min(p.V, v0 + p.chunk);
   const float* z = p.logits + int64_t(row) * p.V;
   float m = -INFINITY, s = 0.0f;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64) void loss_final_kernel(LossArgs p) {
 }
 
 void launch_loss_rows(const LossArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(loss_rows_kernel, dim3(a.nchunks, a.B * a.P), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(loss_rows_kernel, dim3(a.B * a.P, a.nchunks), dim3(256), 0, s, a);
 }
 
 void launch_loss_seq(const LossArgs& a, hipStream_t s) {

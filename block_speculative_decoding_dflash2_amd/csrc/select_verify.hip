@@ -319,7 +319,7 @@ void launch_select(const SelectArgs& a, int tw, hipStream_t s) {
 // grid = (nchunks, B * bs), block = 256: best (value, id) key of one chunk.
 __global__ __launch_bounds__(256) void verify_partial_kernel(VerifyArgs p) {
   __shared__ uint64_t red[4];
-  const int c = blockIdx.x, row = blockIdx.y;
+  const int row = blockIdx.x, c = blockIdx.y;
   const int v0 = c * p.chunk;
   const int v1 = min(p.V, v0 + p.chunk);
   const float* z = p.logits + int64_t(row) * p.V;
@@ -397,7 +397,8 @@ __global__ __launch_bounds__(256) void verify_final_kernel(VerifyArgs p) {
 }
 
 void launch_verify_partial(const VerifyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(verify_partial_kernel, dim3(a.nchunks, a.B * a.bs), dim3(256), 0, s, a);
+  // rows on x (up to 2^31 - 1 blocks), vocabulary chunks (at most 2048) on y
+  hipLaunchKernelGGL(verify_partial_kernel, dim3(a.B * a.bs, a.nchunks), dim3(256), 0, s, a);
 }
 
 void launch_verify_final(const VerifyArgs& a, hipStream_t s) {

@@ -159,9 +159,10 @@ typedef struct dflash2_handle dflash2_handle;
 
 /* Validate the configuration and weight table and build a handle.  Rejects
  * (before any device work, the same rule the NIM page states for draft heads
- * in "Bring Your Own DFlash2 Head"): block_size < 2, num_q_heads not a
- * multiple of num_kv_heads, odd or oversized head_dim, conv_kernel_size
- * outside 1..block_size, conv_group_size that is negative or does not
+ * in "Bring Your Own DFlash2 Head"): block_size outside 2..4096,
+ * max_batch * block_size > 2^30, num_q_heads not a multiple of
+ * num_kv_heads, odd or oversized head_dim, conv_kernel_size outside
+ * 1..block_size, conv_group_size that is negative or does not
  * divide hidden, selector_top_k outside 1..min(64, vocab), selector_rank
  * outside 1..256, mask_token_id outside [0, vocab), an unknown weight_dtype,
  * a null weight (the static conv taps when conv_group_size is 0, the dynamic
@@ -266,7 +267,10 @@ dflash2_status dflash2_select_path_stop(dflash2_handle* handle, hipStream_t stre
                                         int32_t n_max, int32_t* path_idx, int32_t* draft_tokens,
                                         int32_t* draft_lens, float* path_conf, float* path_score);
 
-/* Bytes of device workspace dflash2_verify_accept needs. */
+/* Bytes of device workspace dflash2_verify_accept needs.  Every stateless
+ * step-5 and loss entry point below requires 2 <= block_size <= 4096,
+ * batch >= 1, batch * block_size <= 2^30 and vocab >= 1, else
+ * DFLASH2_ERR_SHAPE. */
 dflash2_status dflash2_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab,
                                              size_t* bytes);
 

@@ -27,10 +27,14 @@ def _inputs(w, tag):
 
 CASES = [("tiny_fp32", {}), ("small_bf16", {}), ("small_fp8", {}),
          ("small_bf16", dict(output_multiplier=0.5, final_logit_softcapping=30.0)),
-         ("dense27b_bf16", {}), ("batched_bf16", {}), ("fp8_b256", {})]
+         ("dense27b_bf16", {}), ("batched_bf16", {}), ("fp8_b256", {}),
+         # 70000 supervised rows: more row blocks than a grid's y or z axis holds
+         ("tiny_fp32", dict(batch=70000, block_size=2, vocab=64))]
+CASE_IDS = ["tiny_fp32", "small_bf16", "small_fp8", "small_bf16_softcap", "dense27b_bf16", "batched_bf16",
+            "fp8_b256", "tiny_fp32_70000_rows"]
 
 
-@pytest.mark.parametrize("name,over", CASES, ids=[f"{n}{'_softcap' if o else ''}" for n, o in CASES])
+@pytest.mark.parametrize("name,over", CASES, ids=CASE_IDS)
 def test_losses_match_oracle(name, over):
     from test_gpu_verify_select import _select_model
     w = synth.get(name).replace(selector_active=True, **over)

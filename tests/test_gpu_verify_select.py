@@ -21,6 +21,7 @@ VERIFY_SHAPES = [
     ("fp8_b256", 256, 8, 151936),
     ("ragged_vocab", 5, 4, 3001),
     ("min_block", 3, 2, 7),
+    ("many_rows", 33000, 2, 16),   # 66000 rows: more row blocks than a grid's y axis holds
 ]
 
 
