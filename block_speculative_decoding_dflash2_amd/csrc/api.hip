@@ -131,10 +131,14 @@ Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
     // epilogue of about kStreamBlockOverhead k; ties go to fewer splits.
     // (Rounding the split count up to fill the slots made grids of 520-560
     // blocks, whose second wave of 8-48 blocks doubled the kernel's time.)
-    int overhead = kStreamBlockOverhead;
+    int overhead = kStreamBlockOverhead, target = kTargetBlocks;
     if (const char* env = std::getenv("DFLASH2_STREAM_BLOCK_OVERHEAD")) {
       const int v = std::atoi(env);
       if (v >= 0 && v <= 65536) overhead = v;
+    }
+    if (const char* env = std::getenv("DFLASH2_STREAM_TARGET_BLOCKS")) {
+      const int v = std::atoi(env);
+      if (v >= 64 && v <= 8192) target = v;
     }
     // Each block's stream is also kept to at most kStreamMaxRowBytes of every
     // weight row: the 5120 x 25600 feature projection measured 55 us with 480
@@ -148,7 +152,7 @@ Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
       const int64_t ks = cdiv(cdiv(K, c), 32) * 32;
       if (cdiv(K, ks) != c) continue;
       const bool capped = ks * wb <= kStreamMaxRowBytes;
-      const double cost = double(cdiv(blocks * c, kTargetBlocks)) * double(ks + overhead);
+      const double cost = double(cdiv(blocks * c, target)) * double(ks + overhead);
       if ((capped && !best_capped) || (capped == best_capped && cost < best_cost * 0.999)) {
         best_cost = cost;
         best_capped = capped;

@@ -75,8 +75,14 @@ __device__ __forceinline__ void lds_load16(const void* g, void* l) {
 // 16-byte chunk permutation of an LDS row
 __device__ __forceinline__ int chunk_perm(int r) { return r ^ (r >> 2); }
 
-template <typename TW, int BM>
+// s_waitcnt immediate: at most vm vector-memory operations outstanding, no
+// LDS/scalar operation outstanding, export count untouched (gfx9 layout:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
+template <typename TW, int BM, int R = 2>
 struct DmaTile {
+  static_assert(R == 2 || R == 3, "two or three stage buffers");
   static constexpr int SW = int(sizeof(TW));
   static constexpr int WROW = kLKT * SW, XROW = kLKT * 2;   // LDS bytes per row and stage
   static constexpr int WBYTES = kLBN * WROW, XBYTES = BM * XROW;
@@ -90,7 +96,8 @@ struct DmaTile {
   // results are never used).  wave must be wave-uniform.
   __device__ __forceinline__ static void run(const bf16_t* __restrict__ X, int64_t ldx, const TW* __restrict__ W,
                                              int64_t ldw, int N, int Mact, int n0, int m0, int nk, int wave,
-                                             char* w0, char* w1, char* x0, char* x1, f32x16 (&acc)[4][FJ]) {
+                                             char* w0, char* w1, char* w2, char* x0, char* x1, char* x2,
+                                             f32x16 (&acc)[4][FJ]) {
     // An empty asm makes the lane index opaque, so the per-lane offsets below
     // are recomputed on every call rather than hoisted out of the caller's
     // tile loop and kept (spilled) across its epilogue.
@@ -191,7 +198,10 @@ struct DmaTile {
     };
     // One stage on (wl, xl), whose step 0 operands are already requested;
     // the next stage is in (wn, xn); after the barrier the loads of stage
-    // kt_load go into (wl, xl), which no wave reads any more.
+    // kt_load go into (wl, xl), which no wave reads any more.  Before the
+    // barrier each wave waits for its loads of the next stage (with three
+    // buffers the loads of the stage after it stay in flight) and for its
+    // reads of this one.
     auto stage = [&](char* wl, char* xl, const char* wn, const char* xn, int kt_load) {
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
@@ -200,8 +210,15 @@ struct DmaTile {
         interleave(nreads(s + 1), 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next stage, and its reads of this one
-      __syncthreads();
+      if constexpr (R == 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      } else {
+        // a workgroup fence would wait for every load in flight; the wait
+        // above covers what the barrier must order (LDS only)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(WLD + XLD));
+        asm volatile("s_barrier" ::: "memory");
+      }
       __builtin_amdgcn_sched_barrier(0);
       load_stage(kt_load, wl, xl);
       prefetch(0, wn, xn);
@@ -209,17 +226,35 @@ struct DmaTile {
       interleave(nreads(0), WLD + XLD);
       __builtin_amdgcn_sched_barrier(0);
     };
-    load_stage(0, w0, x0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    load_stage(min(1, nk - 1), w1, x1);
-    prefetch(0, w0, x0);
+    // Loads past the last stage repeat the last stage, so every stage has
+    // the same loads in flight and the wait counts stay exact.
     int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
-      stage(w0, x0, w1, x1, min(kt + 2, nk - 1));
-      stage(w1, x1, w0, x0, min(kt + 3, nk - 1));
+    if constexpr (R == 2) {
+      load_stage(0, w0, x0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      load_stage(min(1, nk - 1), w1, x1);
+      prefetch(0, w0, x0);
+      for (; kt + 2 <= nk; kt += 2) {
+        stage(w0, x0, w1, x1, min(kt + 2, nk - 1));
+        stage(w1, x1, w0, x0, min(kt + 3, nk - 1));
+      }
+      if (kt < nk) stage(w0, x0, w1, x1, nk - 1);
+    } else {
+      load_stage(0, w0, x0);
+      load_stage(min(1, nk - 1), w1, x1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WLD + XLD));
+      asm volatile("s_barrier" ::: "memory");
+      load_stage(min(2, nk - 1), w2, x2);
+      prefetch(0, w0, x0);
+      for (; kt + 3 <= nk; kt += 3) {
+        stage(w0, x0, w1, x1, min(kt + 3, nk - 1));
+        stage(w1, x1, w2, x2, min(kt + 4, nk - 1));
+        stage(w2, x2, w0, x0, min(kt + 5, nk - 1));
+      }
+      if (kt < nk) stage(w0, x0, w1, x1, nk - 1);
+      if (kt + 1 < nk) stage(w1, x1, w2, x2, nk - 1);
     }
-    if (kt < nk) stage(w0, x0, w1, x1, nk - 1);
     __builtin_amdgcn_s_waitcnt(0);   // the last (repeated) loads have landed before LDS is reused
   }
 };
@@ -283,14 +318,16 @@ __device__ __forceinline__ void sort16_desc(float (&a)[16]) {
 // are staged in LDS by the lanes of rows that have some and inserted into
 // the lane's sorted list of 16; rows whose lanes found nothing keep their
 // list untouched.
-template <typename TW, int BM>
+template <typename TW, int BM, int R>
 __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
-  typedef DmaTile<TW, BM> T;
+  typedef DmaTile<TW, BM, R> T;
   constexpr int FJ = T::FJ, WM = T::WM;
   __shared__ __attribute__((aligned(1024))) char w0[T::WBYTES];
   __shared__ __attribute__((aligned(1024))) char w1[T::WBYTES];
+  __shared__ __attribute__((aligned(1024))) char w2[R == 3 ? T::WBYTES : 16];
   __shared__ __attribute__((aligned(1024))) char x0[T::XBYTES];
   __shared__ __attribute__((aligned(1024))) char x1[T::XBYTES];
+  __shared__ __attribute__((aligned(1024))) char x2[R == 3 ? T::XBYTES : 16];
   __shared__ float inv[BM];
   __shared__ float thr[BM];       // first tile of a run: the bound T
   __shared__ uint64_t thrk[BM];   // the row's current 16th key of the run (0: fewer than 16 so far)
@@ -343,7 +380,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
       vscale4[tid] = sv;
     }
     f32x16 acc[4][FJ];
-    T::run(p.X, p.ldx, W, p.ldw, p.N, Mact, n0, m0, nk, wave, w0, w1, x0, x1, acc);
+    T::run(p.X, p.ldx, W, p.ldw, p.N, Mact, n0, m0, nk, wave, w0, w1, w2, x0, x1, x2, acc);
     // lane (r, h) of wave (wv, wm): value 4 q + e of acc[i][j] is vocabulary id
     // n0 + lb + 32 i + 8 q + e, lb = 128 wv + 4 h, of local row WM wm + 32 j + r.
     // Per-lane values are recomputed per tile (see DmaTile::run).
@@ -692,8 +729,10 @@ template <typename TW>
 static void launch_lm_t(const LmTiledArgs& a, int bm, hipStream_t s) {
   const int blocks = a.nM * a.runs;
   const dim3 grid(unsigned((blocks + 7) / 8 * 8));
-  if (bm == 256) hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 256>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 128>), grid, dim3(256), 0, s, a);
+  // three stage buffers where they fit in LDS (not bf16 with 256 rows)
+  constexpr int R256 = sizeof(TW) == 1 ? 3 : 2;
+  if (bm == 256) hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 256, R256>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 128, 3>), grid, dim3(256), 0, s, a);
 }
 
 void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
