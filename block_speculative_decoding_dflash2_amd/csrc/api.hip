@@ -87,38 +87,47 @@ int weight_bytes(const dflash2_config& c) {
 
 struct Split {
   int splits = 1, k_split = 0;
+  int tile_rows = 0;  // LDS-tiled GEMM: activation rows per block tile
 };
-
-constexpr int kTiledSlots = 512;  // tiled-GEMM blocks resident at once: two per CU on 256 CUs
 
 Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
   Split s;
   if (gemm_tiled_ok(dtype, M, K)) {
-    // compute-bound tiles: pick the split count with the shortest makespan,
-    // counting waves of kTiledSlots resident tiles, each costing its k range
-    // plus a fixed epilogue/prologue cost of about 512 k; ties go to fewer
-    // splits
-    // At most 8 splits by default: more splits only multiply the float32
-    // partial sums the consumers must read back (measured: capping at 8
-    // rather than 16 cut the 256-row workload's linears from 604 to 518 us
-    // per step, and left the 448- and 2048-row ones equal or slightly faster).
-    const int64_t tiles = cdiv(M, tiled_block_rows(M)) * cdiv(N, 256) * groups;
-    int best = 1, max_splits = 8;
+    // compute-bound tiles: the block tile (256 or 128 activation rows) and
+    // split count with the shortest estimated time, counting waves of
+    // resident tiles (256 CUs x tiles per CU), each costing its k range plus
+    // a fixed prologue/epilogue of about 512 k at ~1.2 PF/s of 256-row tiles
+    // (fp8 128-row tiles, two per CU, measured ~7% faster per flop; bf16
+    // 128-row tiles, one per CU, ~20% slower), plus the float32 partial
+    // sums every split writes and its consumer reads back (8 bytes per
+    // output per split at ~5 TB/s); ties go to fewer splits and larger
+    // tiles, at most 8 splits.
+    int max_splits = 8;
     if (const char* env = std::getenv("DFLASH2_TILED_MAX_SPLITS")) {
       const int v = std::atoi(env);
       if (v >= 1 && v <= 16) max_splits = v;
     }
     double best_cost = 1e300;
-    for (int S = 1; S <= max_splits; ++S) {
-      const int64_t ks = cdiv(cdiv(K, S), 64) * 64;
-      if (cdiv(K, ks) != S) continue;
-      const double cost = double(cdiv(tiles * S, kTiledSlots)) * double(ks + 512);
-      if (cost < best_cost * 0.97) {
-        best_cost = cost;
-        best = S;
+    for (int bm : {256, 128}) {
+      const TiledShape sh = tiled_shape(dtype, M, bm);
+      if (sh.bm != bm) continue;
+      const int64_t tiles = cdiv(M, sh.bm) * cdiv(N, 256) * groups;
+      const int64_t slots = 256 * int64_t(sh.per_cu);
+      const double eff = sh.bm == 256 ? 1.0 : (sh.per_cu == 2 ? 0.93 : 1.2);
+      const double us_per_k = 2.0 * 256.0 * sh.bm * sh.per_cu / 4.7e6 * eff;  // one tile, per k, in us
+      for (int S = 1; S <= max_splits; ++S) {
+        const int64_t ks = cdiv(cdiv(K, S), 64) * 64;
+        if (cdiv(K, ks) != S) continue;
+        const double cost = double(cdiv(tiles * S, slots)) * double(ks + 512) * us_per_k +
+                            8.0 * S * double(M) * N * groups / 5e6;
+        if (cost < best_cost * 0.97) {
+          best_cost = cost;
+          s.splits = S;
+          s.tile_rows = sh.bm;
+        }
       }
     }
-    s.k_split = int(cdiv(cdiv(K, best), 64) * 64);
+    s.k_split = int(cdiv(cdiv(K, s.splits), 64) * 64);
     s.splits = int(cdiv(K, s.k_split));
     return s;
   }
@@ -439,7 +448,7 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
     a.X = X; a.ldx = ldx; a.W = W; a.ldw = K; a.scale = scale;
     a.P = out; a.ldp = N; a.split_stride = int64_t(M) * N;
     a.M = M; a.N = N; a.K = K; a.M_dev = M_dev;
-    a.splits = sp.splits; a.k_split = sp.k_split; a.groups = 1;
+    a.splits = sp.splits; a.k_split = sp.k_split; a.groups = 1; a.tile_rows = sp.tile_rows;
     const int64_t bytes = int64_t(N) * K * wb + (scale ? int64_t(N) * 4 : 0) + int64_t(M) * K * ab +
                           int64_t(M) * N * 4;
     const bool fused = epi && gemm_epi_fusable(dt, a);
@@ -500,7 +509,7 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
       a.X = nbuf; a.ldx = H; a.ldw = H;
       a.P = parts + l0 * lstride; a.ldp = kvd; a.split_stride = int64_t(P.Mn) * kvd;
       a.M = P.Mn; a.N = kvd; a.K = H; a.M_dev = rows_dev;
-      a.splits = P.kv.splits; a.k_split = P.kv.k_split;
+      a.splits = P.kv.splits; a.k_split = P.kv.k_split; a.tile_rows = P.kv.tile_rows;
       a.groups = ng; a.group_stride = lstride;
       for (int g = 0; g < ng; ++g) {
         const dflash2_layer_weights& L = handle->layers[l0 + g];

@@ -45,6 +45,7 @@ struct GemmArgs {
   const float* Sg[kMaxGroups];
   int64_t group_stride;
   GemmEpi epi;                    // EPI_NONE: write partial sums
+  int tile_rows;                  // LDS-tiled path: rows per block tile (0: default for M)
 };
 
 struct LmHeadArgs {
@@ -186,7 +187,11 @@ int gemm_rows_per_block(int weight_dtype, int M);
 bool gemm_tiled_ok(int weight_dtype, int M, int K);
 bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k);
 int lmhead_tiled_lists(int M, int V);
-int tiled_block_rows(int M);
+// Block tile of the LDS-tiled GEMM: bm activation rows x 256 weight rows,
+// per_cu blocks resident per CU.  bm = the requested 256 or 128 (0: the
+// default for M rows); DFLASH2_TILED_BM overrides it.
+struct TiledShape { int bm, per_cu; };
+TiledShape tiled_shape(int weight_dtype, int M, int bm);
 void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s);
 void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s);
 void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s);

@@ -315,6 +315,24 @@ def test_draft_tiled_single_split(name, monkeypatch):
         g.close()
 
 
+@pytest.mark.parametrize("name", ["medium_bf16", "medium_fp8"])
+@pytest.mark.parametrize("splits", ["1", "8"])
+def test_draft_tiled_128_row_tiles(name, splits, monkeypatch):
+    """Tiled GEMMs on 128-row block tiles (fp8: two blocks per CU with two
+    stage buffers; bf16: three stage buffers), ragged last row tile, with
+    one K split (SwiGLU and QKV epilogues) and with the planner's splits
+    (partial sums): same checks as the default 256-row tiles."""
+    monkeypatch.setenv("DFLASH2_TILED_BM", "128")
+    monkeypatch.setenv("DFLASH2_TILED_MAX_SPLITS", splits)
+    w = synth.get(name)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
+
+
 @pytest.mark.parametrize("name,window", [("small_bf16", 64), ("medium_fp8", 100), ("small_fp32", 33),
                                          ("tiny_fp32", 8)])
 def test_draft_sliding_window(name, window):
