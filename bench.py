@@ -2,9 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--extra NAMES]
 
-One step = dflash2_draft_block (context append, block forward, lm_head +
-top-k) + dflash2_select_path + dflash2_verify_accept over one batch of
-seeded synthetic inputs already resident in HBM.  Consecutive steps rotate
+One step = dflash2_draft_select (context append, block forward, lm_head +
+top-k, and the path selector, whose kernel also merges the candidates;
+the same results as dflash2_draft_block + dflash2_select_path) +
+dflash2_verify_accept over one batch of seeded synthetic inputs already
+resident in HBM.  Consecutive steps rotate
 over three sets of input and cache buffers (taps, K/V caches, verifier
 logits), so the 256 MB Infinity Cache cannot serve one step's inputs from
 the previous step.  Default workload: the 27B-class single-sequence draft
@@ -217,13 +219,20 @@ def run_workload(name, args, primary: bool):
     def step():
         s = sets[it[0] % ROTATE]
         it[0] += 1
-        model.draft_block(anchors, s["taps"], offsets, ctx_lens, max_new, s["kc"], s["vc"], workspace=ws,
-                          topk_ids=topk_ids, topk_vals=topk_vals, debug_logits=dlogits)
+        if dlogits is None and lens is None:
+            # steps 1-4 in one call: the candidate merge runs in the selector's kernel
+            model.draft_select(anchors, s["taps"], offsets, ctx_lens, max_new, s["kc"], s["vc"], workspace=ws,
+                               topk_ids=topk_ids, topk_vals=topk_vals, path_idx=path, draft_tokens=drafts,
+                               want_score=False)
+        else:
+            model.draft_block(anchors, s["taps"], offsets, ctx_lens, max_new, s["kc"], s["vc"], workspace=ws,
+                              topk_ids=topk_ids, topk_vals=topk_vals, debug_logits=dlogits)
         if dlogits is not None:
             model.draft_losses(anchors, labels, dlogits, topk_ids, topk_vals, gamma, wsel, losses=loss_out)
         if lens is None:
-            model.select_path(anchors, topk_ids, topk_vals, path_idx=path, draft_tokens=drafts,
-                              want_score=False)
+            if dlogits is not None:
+                model.select_path(anchors, topk_ids, topk_vals, path_idx=path, draft_tokens=drafts,
+                                  want_score=False)
         else:
             model.select_path_stop(anchors, topk_ids, topk_vals, p_min=args.p_min, path_idx=path,
                                    draft_tokens=drafts, draft_lens=lens)

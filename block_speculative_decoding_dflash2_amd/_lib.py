@@ -43,7 +43,7 @@ class dflash2_weights(ctypes.Structure):
 
 KERNEL_KINDS = ("gemm", "lmhead_topk", "topk_merge", "norm", "qkv_epilogue", "kv_append", "swiglu",
                 "attention", "attn_combine", "select", "verify_partial", "verify_final", "sample_rows",
-                "sample_pick", "loss_rows", "loss_seq")
+                "sample_pick", "loss_rows", "loss_seq", "merge_select")
 
 
 class dflash2_trace_entry(ctypes.Structure):
@@ -78,6 +78,8 @@ def _load():
         "dflash2_workspace_size": ([vp, c_int32, c_int64, POINTER(c_size_t)], c_int32),
         "dflash2_draft_block": ([vp, vp, c_int32, i32p, vp, i32p, i32p, c_int64, vp, vp, i32p, f32p,
                                  f32p, f32p, vp, c_size_t], c_int32),
+        "dflash2_draft_select": ([vp, vp, c_int32, i32p, vp, i32p, i32p, c_int64, vp, vp, i32p, f32p, i32p,
+                                  i32p, f32p, f32p, vp, c_size_t], c_int32),
         "dflash2_select_path": ([vp, vp, c_int32, i32p, i32p, f32p, i32p, i32p, f32p, f32p], c_int32),
         "dflash2_select_path_stop": ([vp, vp, c_int32, i32p, i32p, f32p, c_float, c_int32, c_int32, i32p, i32p,
                                       i32p, f32p, f32p], c_int32),
@@ -107,6 +109,7 @@ def _load():
 
 lib = _load()
 EXPORTED = ("dflash2_create", "dflash2_destroy", "dflash2_workspace_size", "dflash2_draft_block",
+            "dflash2_draft_select",
             "dflash2_select_path", "dflash2_select_path_stop", "dflash2_verify_workspace_size",
             "dflash2_verify_accept", "dflash2_verify_accept_noalloc", "dflash2_verify_sample_workspace_size",
             "dflash2_verify_sample",
@@ -162,6 +165,14 @@ def dflash2_draft_block(handle, stream, batch, anchor_ids, new_taps, new_offsets
     _check(lib.dflash2_draft_block(handle, stream, batch, anchor_ids, new_taps, new_offsets, ctx_lens,
                                    max_new_rows, k_cache, v_cache, topk_ids, topk_vals, debug_logits,
                                    debug_hidden, workspace, workspace_bytes))
+
+
+def dflash2_draft_select(handle, stream, batch, anchor_ids, new_taps, new_offsets, ctx_lens,
+                         max_new_rows, k_cache, v_cache, topk_ids, topk_vals, path_idx, draft_tokens,
+                         path_score, debug_logits, workspace, workspace_bytes) -> None:
+    _check(lib.dflash2_draft_select(handle, stream, batch, anchor_ids, new_taps, new_offsets, ctx_lens,
+                                    max_new_rows, k_cache, v_cache, topk_ids, topk_vals, path_idx, draft_tokens,
+                                    path_score, debug_logits, workspace, workspace_bytes))
 
 
 def dflash2_select_path(handle, stream, batch, anchor_ids, topk_ids, topk_vals, path_idx,

@@ -221,7 +221,7 @@ Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
   const int gk = c.conv_group_size > 0 ? H / c.conv_group_size * c.conv_kernel_size : 0;
   p.dconv = gk > 0 ? plan_split(dt, p.M, gk, H) : Split{1, H};
   p.attn = plan_attn(c, B);
-  p.groups = int(cdiv(c.vocab, 256));
+  p.groups = int(cdiv(c.vocab, kLmGroupIds));
   const size_t ab = act_bytes(c);
   size_t parts = 0;
   auto upd = [&](size_t v) { parts = std::max(parts, v); };
@@ -271,6 +271,11 @@ const void* byte_offset(const void* p, int64_t bytes) {
 }
 
 constexpr size_t kSelectLds = 156 * 1024;  // one window covers every position at the configs here
+dflash2_status select_impl(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                           const int32_t* anchor_ids, const int32_t* topk_ids, const float* topk_vals,
+                           int32_t* path_idx, int32_t* draft_tokens, float* path_score, float* debug_pair,
+                           float p_min, int32_t n_min, int32_t n_max, int32_t* draft_lens,
+                           float* path_conf, const char* name);
 
 }  // namespace
 
@@ -395,13 +400,17 @@ dflash2_status dflash2_workspace_size(const dflash2_handle* handle, int32_t batc
   return ok();
 }
 
-dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, int32_t batch,
-                                   const int32_t* anchor_ids, const void* new_taps,
-                                   const int32_t* new_offsets, const int32_t* ctx_lens,
-                                   int64_t max_new_rows, void* k_cache, void* v_cache,
-                                   int32_t* topk_ids, float* topk_vals, float* debug_logits,
-                                   float* debug_hidden, void* workspace, size_t workspace_bytes) {
+// Steps 1-3, and with path_idx non-null step 4 too (the candidate merge then
+// runs inside the selector's kernel when k <= 16).
+static dflash2_status draft_impl(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                 const int32_t* anchor_ids, const void* new_taps,
+                                 const int32_t* new_offsets, const int32_t* ctx_lens,
+                                 int64_t max_new_rows, void* k_cache, void* v_cache,
+                                 int32_t* topk_ids, float* topk_vals, float* debug_logits,
+                                 float* debug_hidden, void* workspace, size_t workspace_bytes,
+                                 int32_t* path_idx, int32_t* draft_tokens, float* path_score) {
   if (!handle) return fail(DFLASH2_ERR_INVALID_ARG, "draft_block: null handle");
+  if (path_idx && !draft_tokens) return fail(DFLASH2_ERR_INVALID_ARG, "draft_select: null draft_tokens");
   const dflash2_config& c = handle->cfg;
   if (batch < 1 || batch > c.max_batch)
     return fail(DFLASH2_ERR_SHAPE, "draft_block: batch %d outside 1..max_batch %d", batch, c.max_batch);
@@ -625,16 +634,66 @@ dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, i
   if (lmhead_tiled_ok(dt, P.Mh, H, c.selector_top_k)) {
     ma.glen = 16;
     ma.count = lmhead_tiled_lists(P.Mh, c.vocab) * 16;
+    ma.lstride = 16; ma.kstride = 1;
   } else {
     ma.glen = c.selector_top_k;
     ma.count = P.groups * c.selector_top_k;
+    ma.lstride = 1; ma.kstride = P.groups;
   }
   ma.M_dev = nullptr; ma.ids = topk_ids; ma.vals = topk_vals;
   ma.multiplier = c.output_multiplier; ma.softcap = c.final_logit_softcapping;
+  if (path_idx && c.selector_top_k <= 16 && ma.count / ma.glen <= 64) {
+    // ---- 4. candidate merge + path selector in one launch: the selector's
+    // kernel merges the (at most 64) sorted lists of each row itself.  With
+    // more lists (the weight-streaming lm_head writes one per 128 ids) the
+    // merge keeps its own kernel: one wave per row cannot fold them as fast
+    // as one block per row does.
+    SelectArgs a{};
+    a.cand = ma.cand; a.count = ma.count; a.glen = ma.glen; a.lstride = ma.lstride; a.kstride = ma.kstride;
+    a.anchors = anchor_ids; a.ids = topk_ids; a.vals = topk_vals;
+    a.tl = handle->w.sel_tl; a.tr = handle->w.sel_tr;
+    a.B = batch; a.P = c.block_size - 1; a.k = c.selector_top_k; a.r = c.selector_rank; a.V = c.vocab;
+    a.path = path_idx; a.drafts = draft_tokens; a.score = path_score;
+    a.multiplier = ma.multiplier; a.softcap = ma.softcap; a.ids_out = topk_ids; a.vals_out = topk_vals;
+    const int64_t pairs = int64_t(batch) * (int64_t(a.P - 1) * a.k * a.k + a.k);
+    const int64_t bytes = int64_t(P.Mh) * a.count * 8 + int64_t(P.Mh) * a.k * 8 +
+                          int64_t(batch) * (a.P * a.k + 1) * 2 * a.r * 4 + int64_t(batch) * a.P * 8;
+    traced(stream, DFLASH2_K_MERGE_SELECT, bytes, 2 * pairs * a.r,
+           [&] { launch_select(a, select_window(a.k, a.r, a.P, kSelectLds), stream); });
+    if ((st = check_launch("draft_select/lm_head")) != DFLASH2_OK) return st;
+    return ok();
+  }
   traced(stream, DFLASH2_K_TOPK_MERGE, int64_t(P.Mh) * ma.count * 8 + int64_t(P.Mh) * ma.k * 8, 0,
          [&] { launch_topk_merge(ma, stream); });
   if ((st = check_launch("draft_block/lm_head")) != DFLASH2_OK) return st;
+  if (path_idx) return select_impl(handle, stream, batch, anchor_ids, topk_ids, topk_vals, path_idx, draft_tokens,
+                                   path_score, nullptr, 0.0f, 0, 0, nullptr, nullptr, "draft_select");
   return ok();
+}
+
+dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                   const int32_t* anchor_ids, const void* new_taps,
+                                   const int32_t* new_offsets, const int32_t* ctx_lens,
+                                   int64_t max_new_rows, void* k_cache, void* v_cache,
+                                   int32_t* topk_ids, float* topk_vals, float* debug_logits,
+                                   float* debug_hidden, void* workspace, size_t workspace_bytes) {
+  return draft_impl(handle, stream, batch, anchor_ids, new_taps, new_offsets, ctx_lens, max_new_rows, k_cache,
+                    v_cache, topk_ids, topk_vals, debug_logits, debug_hidden, workspace, workspace_bytes, nullptr,
+                    nullptr, nullptr);
+}
+
+dflash2_status dflash2_draft_select(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                    const int32_t* anchor_ids, const void* new_taps,
+                                    const int32_t* new_offsets, const int32_t* ctx_lens,
+                                    int64_t max_new_rows, void* k_cache, void* v_cache, int32_t* topk_ids,
+                                    float* topk_vals, int32_t* path_idx, int32_t* draft_tokens,
+                                    float* path_score, float* debug_logits, void* workspace,
+                                    size_t workspace_bytes) {
+  if (!path_idx) return fail(DFLASH2_ERR_INVALID_ARG, "draft_select: null path_idx");
+  const dflash2_status st = draft_impl(handle, stream, batch, anchor_ids, new_taps, new_offsets, ctx_lens,
+                                       max_new_rows, k_cache, v_cache, topk_ids, topk_vals, debug_logits, nullptr,
+                                       workspace, workspace_bytes, path_idx, draft_tokens, path_score);
+  return st == DFLASH2_OK ? ok() : st;
 }
 
 }  // extern "C"

@@ -211,41 +211,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 }
 
 // lm_head with the per-vocabulary-group top-k fused into the epilogue.
-// grid = (ceil(V / 256), ceil(M / 16)); each block computes the logits of 256
-// vocabulary rows for 16 activation rows over the full K, stages them in LDS,
-// and keeps each activation row's k best (value desc, id asc) as 64-bit keys.
+// grid = (ceil(V / kLmGroupIds), ceil(M / 16)); each block computes the
+// logits of 128 vocabulary rows (32 per wave) for 16 activation rows over
+// the full K, stages them in LDS, and keeps each activation row's k best
+// (value desc, id asc) as 64-bit keys.  (256 rows per block in two passes
+// of 32 rows per wave measured slower at the 27B workload: 292 against
+// 272-278 us per step; each pass drained and refilled the load ring.)
 template <typename TA, typename TW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void lmhead_topk_kernel(LmHeadArgs p) {
-  constexpr int RT = 2;  // two passes of 32 rows per wave: 64 rows, 256 per block
+  constexpr int RT = 2;  // 32 rows per wave, 128 per block
+  constexpr int G = kLmGroupIds;
+  static_assert(G == 4 * 16 * RT, "one pass of 16 RT rows per wave");
   typedef GemmTile<TA, TW, RT, 1, 2> Tile;
   __shared__ __attribute__((aligned(16))) char lds[4][Tile::LDS_BYTES];
-  __shared__ float logits[16][256 + 4];
+  __shared__ float logits[16][G + 4];
   const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
   const int m0 = blockIdx.y * 16;
   if (m0 >= Mact) return;
   const int wave = threadIdx.x / WAVE;
   const int lane = threadIdx.x & (WAVE - 1);
   const int r = lane & 15, g = lane >> 4;
-  const int vbase = blockIdx.x * 256;
-  f32x4 acc[2 * RT][1];
+  const int vbase = blockIdx.x * G;
+  f32x4 acc[RT][1];
+  const int n0 = vbase + wave * 16 * RT;
+  if (n0 < p.N) {
+    Tile::run(static_cast<const TA*>(p.X), p.ldx, static_cast<const TW*>(p.W), p.ldw, p.N, Mact, n0, m0, 0,
+              p.K, acc, lds[wave]);
+  } else {
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int n0 = vbase + wave * 64 + pass * 16 * RT;
-    f32x4 part[RT][1];
-    if (n0 < p.N) {
-      Tile::run(static_cast<const TA*>(p.X), p.ldx, static_cast<const TW*>(p.W), p.ldw, p.N, Mact, n0, m0,
-                0, p.K, part, lds[wave]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < RT; ++i) part[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int i = 0; i < RT; ++i) acc[pass * RT + i][0] = part[i][0];
+    for (int i = 0; i < RT; ++i) acc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float inv = row_inv_rms(p.rs, min(m0 + r, Mact - 1));
 #pragma unroll
-  for (int i = 0; i < 2 * RT; ++i) {
-    const int nl = wave * 64 + 16 * i + 4 * g;  // local vocab index
+  for (int i = 0; i < RT; ++i) {
+    const int nl = wave * 16 * RT + 16 * i + 4 * g;  // local vocab index
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int n = vbase + nl + e;
@@ -260,27 +259,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
   }
   __syncthreads();
   // each wave ranks 4 of the 16 rows
+  constexpr int KPL = G / WAVE;  // keys per lane
   for (int rr = 0; rr < 4; ++rr) {
     const int row = wave * 4 + rr;
     const int m = m0 + row;
     if (m >= Mact) break;
-    uint64_t key[4];
+    uint64_t key[KPL];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int nl = lane + 64 * e;
+    for (int e = 0; e < KPL; ++e) {
+      const int nl = lane + WAVE * e;
       const int n = vbase + nl;
       key[e] = n < p.N ? rank_key(logits[row][nl], uint32_t(n)) : 0ull;
     }
-    uint64_t* out = p.cand + (int64_t(m) * p.groups + blockIdx.x) * p.k;
+    // key t of this group at (m k + t) groups + group: the merge's lanes
+    // then read consecutive groups with coalesced loads
+    uint64_t* out = p.cand + int64_t(m) * p.k * p.groups + blockIdx.x;
     for (int t = 0; t < p.k; ++t) {
       uint64_t best = key[0];
 #pragma unroll
-      for (int e = 1; e < 4; ++e) best = key[e] > best ? key[e] : best;
+      for (int e = 1; e < KPL; ++e) best = key[e] > best ? key[e] : best;
       best = wave_max_u64(best);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < KPL; ++e)
         if (key[e] == best) key[e] = 0ull;
-      if (lane == 0) out[t] = best;
+      if (lane == 0) out[int64_t(t) * p.groups] = best;
     }
   }
 }
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(TopkMergeArgs p) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const int src = KMAX - 1 - j;                 // reversed: ascending
-      dst[j] = (gi < groups && src < p.glen) ? c[int64_t(gi) * p.glen + src] : 0ull;
+      dst[j] = (gi < groups && src < p.glen) ? c[int64_t(gi) * p.lstride + int64_t(src) * p.kstride] : 0ull;
     }
   };
   uint64_t nxt[KMAX];

@@ -48,22 +48,27 @@ struct GemmArgs {
   int tile_rows;                  // LDS-tiled path: rows per block tile (0: default for M)
 };
 
+// Vocabulary ids per block (and per candidate list) of the weight-streaming
+// lm_head.
+constexpr int kLmGroupIds = 128;
+
 struct LmHeadArgs {
   const void* X; int64_t ldx;     // [M][K] act
   const void* W; int64_t ldw;     // [V][K]
   const float* scale;             // [V] or null
   int M, N, K;                    // N = vocab
   const int32_t* M_dev;
-  int groups;                     // ceil(V / 256)
+  int groups;                     // ceil(V / kLmGroupIds)
   int k;                          // candidates per group and row
-  uint64_t* cand;                 // [M][groups][k] ranking keys
+  uint64_t* cand;                 // [M][k][groups] ranking keys (key t of group g at t * groups + g)
   float* debug_logits;            // [M][V] or null
   RowScale rs;
 };
 
 struct TopkMergeArgs {
-  const uint64_t* cand;           // [M][count]: count / glen sorted lists of glen keys
-  int count, glen, M, k;
+  const uint64_t* cand;           // [M][count]: count / glen sorted lists of glen keys,
+  int count, glen, M, k;          //   key j of list g at g * lstride + j * kstride
+  int lstride, kstride;
   const int32_t* M_dev;
   int32_t* ids; float* vals;      // [M][k]
   float multiplier, softcap;
@@ -146,6 +151,15 @@ struct SelectArgs {
   // (computed when lens or conf is non-null)
   float p_min; int n_min, n_max;
   int32_t* lens; float* conf;
+  // Fused candidate merge (cand != null; k <= 16, at most 64 lists per
+  // row): before the selector, the block reduces each of its rows' count /
+  // glen sorted candidate lists of
+  // glen keys (cand [B*P][count], layout as in TopkMergeArgs) to the k
+  // best, applies the logit transform and writes them to ids_out /
+  // vals_out (the ids / vals read above, same addresses).
+  const uint64_t* cand; int count, glen, lstride, kstride;
+  float multiplier, softcap;
+  int32_t* ids_out; float* vals_out;
 };
 
 struct VerifyArgs {

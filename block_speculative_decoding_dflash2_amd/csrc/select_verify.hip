@@ -55,6 +55,12 @@ __device__ __forceinline__ void pair_dot2x2(const float* __restrict__ a0, const 
 
 __host__ __device__ int select_row_stride(int r) { return (r + 3) / 4 * 4 + 4; }
 
+// 4-byte words of the selector's LDS (listed below), rounded up to even.
+__host__ __device__ inline int select_lds_words(int k, int r, int P, int tw) {
+  const int w = 2 * tw * k * select_row_stride(r) + tw * k * k + k + P * k + 2 * P + 3 * tw * k;
+  return (w + 1) & ~1;
+}
+
 // One block of kSelThreads (1024) threads per sequence.  Pair scores depend
 // only on the candidate ids, so a window of `tw` transitions is done at once:
 // the table rows of its candidates are staged in LDS, all its pair scores are
@@ -84,6 +90,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs p, int t
   const float* vals = p.vals + int64_t(b) * P * k;
   const int V = p.V;
   const int anchor = p.anchors[b];
+  if (p.cand) {
+    // ---- fused candidate merge (at most 64 sorted lists per row): one wave
+    // per row, lane l holding list l in registers; each of the k rounds
+    // takes the largest head (wave maximum; keys are unique) and the lane
+    // that held it shifts its list by one.  The result is that row's k best
+    // keys, as the separate merge kernel finds them.
+    const int wave = tid / WAVE, lane = tid & (WAVE - 1);
+    const int nlists = p.count / p.glen;
+    for (int t = wave; t < P; t += kSelThreads / WAVE) {
+      const uint64_t* c = p.cand + (int64_t(b) * P + t) * p.count;
+      uint64_t L[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        L[j] = (lane < nlists && j < p.glen) ? c[int64_t(lane) * p.lstride + int64_t(j) * p.kstride] : 0ull;
+      for (int j = 0; j < k; ++j) {
+        const uint64_t best = wave_max_u64(L[0]);
+        const bool mine = L[0] == best && best != 0ull;
+#pragma unroll
+        for (int q = 0; q < 15; ++q) L[q] = mine ? L[q + 1] : L[q];
+        L[15] = mine ? 0ull : L[15];
+        if (lane == 0) {
+          float z = p.multiplier * key_val(best);
+          if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
+          p.ids_out[(int64_t(b) * P + t) * k + j] = int32_t(key_id(best));
+          p.vals_out[(int64_t(b) * P + t) * k + j] = z;
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   for (int t0 = 0; t0 < P; t0 += tw) {
     const int nt = min(tw, P - t0);
@@ -308,12 +344,11 @@ int select_window(int k, int r, int P, size_t budget) {
   return int(std::min<size_t>(size_t(P), (budget - fixed) / per));
 }
 
-static size_t select_lds_bytes(int k, int r, int P, int tw) {
-  return size_t(2 * tw * k * select_row_stride(r) + tw * k * k + k + P * k + 2 * P + 3 * tw * k) * 4;
-}
+static size_t select_lds_bytes(int k, int r, int P, int tw) { return size_t(select_lds_words(k, r, P, tw)) * 4; }
 
 void launch_select(const SelectArgs& a, int tw, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(kSelThreads), select_lds_bytes(a.k, a.r, a.P, tw), s, a, tw);
+  hipLaunchKernelGGL(select_kernel, dim3(a.B), dim3(kSelThreads), select_lds_bytes(a.k, a.r, a.P, tw),
+                     s, a, tw);
 }
 
 // grid = (nchunks, B * bs), block = 256: best (value, id) key of one chunk.

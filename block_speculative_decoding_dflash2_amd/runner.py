@@ -151,6 +151,37 @@ class DFlash2:
                               ptr(dh), ptr(workspace), workspace.numel())
         return {"topk_ids": topk_ids, "topk_vals": topk_vals, "debug_logits": dl, "debug_hidden": dh}
 
+    def draft_select(self, anchors, taps, offsets, ctx_lens, max_new_rows, k_cache, v_cache,
+                     workspace=None, topk_ids=None, topk_vals=None, path_idx=None, draft_tokens=None,
+                     want_score=True, debug_logits=False, stream=None):
+        """draft_block followed by select_path in one call (the candidate
+        merge runs inside the selector's kernel)."""
+        c = self.cfg
+        B = anchors.numel()
+        P, k = c["block_size"] - 1, c["selector_top_k"]
+        dev = self.device
+        if topk_ids is None:
+            topk_ids = torch.empty((B, P, k), dtype=torch.int32, device=dev)
+        if topk_vals is None:
+            topk_vals = torch.empty((B, P, k), dtype=torch.float32, device=dev)
+        if path_idx is None:
+            path_idx = torch.empty((B, P), dtype=torch.int32, device=dev)
+        if draft_tokens is None:
+            draft_tokens = torch.empty((B, P), dtype=torch.int32, device=dev)
+        score = torch.empty((B,), dtype=torch.float32, device=dev) if want_score else None
+        if isinstance(debug_logits, torch.Tensor):
+            dl = debug_logits
+        else:
+            dl = torch.empty((B, P, c["vocab"]), dtype=torch.float32, device=dev) if debug_logits else None
+        if workspace is None:
+            workspace = self.workspace(B, max_new_rows)
+        L.dflash2_draft_select(self.handle, current_stream() if stream is None else stream, B,
+                               ptr(anchors), ptr(taps), ptr(offsets), ptr(ctx_lens), int(max_new_rows),
+                               ptr(k_cache), ptr(v_cache), ptr(topk_ids), ptr(topk_vals), ptr(path_idx),
+                               ptr(draft_tokens), ptr(score), ptr(dl), ptr(workspace), workspace.numel())
+        return {"topk_ids": topk_ids, "topk_vals": topk_vals, "path": path_idx, "drafts": draft_tokens,
+                "score": score, "debug_logits": dl}
+
     def select_path(self, anchors, topk_ids, topk_vals, debug_pair=False, want_score=True,
                     path_idx=None, draft_tokens=None, stream=None):
         c = self.cfg

@@ -267,6 +267,24 @@ dflash2_status dflash2_select_path_stop(dflash2_handle* handle, hipStream_t stre
                                         int32_t n_max, int32_t* path_idx, int32_t* draft_tokens,
                                         int32_t* draft_lens, float* path_conf, float* path_score);
 
+/* Steps 1-4 in one call (NeMo AutoModel page, "Variants", row DFlash 2:
+ * each position's top-k candidates and one path through them): exactly
+ * dflash2_draft_block followed by dflash2_select_path on its outputs, with
+ * the same arguments and results (topk_ids / topk_vals are still written),
+ * except that the per-row candidate merge runs inside the selector's
+ * kernel, one launch instead of two, when selector_top_k <= 16 and the
+ * lm_head left at most 64 candidate lists per row (the LDS-tiled lm_head
+ * of more than 64 rows, or a vocabulary of at most 8192 ids).
+ * debug_hidden and debug_pair are not offered; path_score may be null.
+ * Workspace: dflash2_workspace_size, as for dflash2_draft_block. */
+dflash2_status dflash2_draft_select(dflash2_handle* handle, hipStream_t stream, int32_t batch,
+                                    const int32_t* anchor_ids, const void* new_taps,
+                                    const int32_t* new_offsets, const int32_t* ctx_lens,
+                                    int64_t max_new_rows, void* k_cache, void* v_cache, int32_t* topk_ids,
+                                    float* topk_vals, int32_t* path_idx, int32_t* draft_tokens,
+                                    float* path_score, float* debug_logits, void* workspace,
+                                    size_t workspace_bytes);
+
 /* Bytes of device workspace dflash2_verify_accept needs.  Every stateless
  * step-5 and loss entry point below requires 2 <= block_size <= 4096,
  * batch >= 1, batch * block_size <= 2^30 and vocab >= 1, else
@@ -417,7 +435,8 @@ typedef enum {
   DFLASH2_K_SAMPLE_ROWS = 12,  /* sampled verification: per-row truncation */
   DFLASH2_K_SAMPLE_PICK = 13,  /* sampled verification: accept walk + draw */
   DFLASH2_K_LOSS_ROWS = 14,    /* forward losses: per-chunk logsumexp       */
-  DFLASH2_K_LOSS_SEQ = 15      /* forward losses: per-slot terms and totals */
+  DFLASH2_K_LOSS_SEQ = 15,     /* forward losses: per-slot terms and totals */
+  DFLASH2_K_MERGE_SELECT = 16  /* dflash2_draft_select: candidate merge + selector */
 } dflash2_kernel_kind;
 
 typedef struct {

@@ -112,6 +112,20 @@ void run_shape(const Shape& s) {
         ++g_fail;
       }
     }
+    {
+      size_t ws = 0;
+      expect(dflash2_workspace_size(h, B, s.new_rows, &ws), DFLASH2_OK, "workspace_size");
+      for (int dl = 0; dl < 2; ++dl)
+        expect(dflash2_draft_select(h, st, B, dev<int32_t>(1), dev<void>(2), dev<int32_t>(3), dev<int32_t>(4),
+                                    s.new_rows, dev<void>(5), dev<void>(6), dev<int32_t>(7), dev<float>(8),
+                                    dev<int32_t>(9), dev<int32_t>(10), dl ? dev<float>(11) : nullptr,
+                                    dl ? dev<float>(12) : nullptr, dev<void>(13), ws),
+               DFLASH2_OK, "draft_select");
+      expect(dflash2_draft_select(h, st, B, dev<int32_t>(1), dev<void>(2), dev<int32_t>(3), dev<int32_t>(4),
+                                  s.new_rows, dev<void>(5), dev<void>(6), dev<int32_t>(7), dev<float>(8), nullptr,
+                                  dev<int32_t>(10), nullptr, nullptr, dev<void>(13), ws),
+             DFLASH2_ERR_INVALID_ARG, "draft_select null path");
+    }
     expect(dflash2_select_path(h, st, B, dev<int32_t>(1), dev<int32_t>(2), dev<float>(3), dev<int32_t>(4),
                                dev<int32_t>(5), dev<float>(6), dev<float>(7)),
            DFLASH2_OK, "select_path");

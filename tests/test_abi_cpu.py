@@ -172,6 +172,17 @@ def test_workspace_size_and_draft_argument_errors():
         with pytest.raises(L.DFlash2Error) as e:
             L.dflash2_select_path_stop(h, None, 3, p, p, p, 0.1, 0, 7, p, p, p, None, None)
         assert e.value.status == L.DFLASH2_ERR_SHAPE
+        # draft_select: the draft_block checks, plus path and draft outputs required
+        for path, drafts in ((None, p), (p, None)):
+            with pytest.raises(L.DFlash2Error) as e:
+                L.dflash2_draft_select(h, None, 1, p, p, p, p, 32, p, p, p, p, path, drafts, None, None, p, n1)
+            assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_draft_select(h, None, 1, p, p, p, p, 32, p, p, p, p, p, p, None, None, p, n1 - 1)
+        assert e.value.status == L.DFLASH2_ERR_WORKSPACE
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_draft_select(h, None, 2, p, p, p, p, 32, p, p, p, p, p, p, None, None, p, n1)
+        assert e.value.status == L.DFLASH2_ERR_SHAPE
     finally:
         L.dflash2_destroy(h)
 
