@@ -42,8 +42,8 @@ def log(msg):
 # Sources that define each traced kernel kind (its kernel code, device
 # helpers and argument structs).
 KERNEL_SOURCES = {
-    "gemm": ["gemm.hip", "gemm_tiled.hip", "common.h", "kernels.h"],
-    "lmhead_topk": ["gemm.hip", "lmhead_tiled.hip", "common.h", "kernels.h"],
+    "gemm": ["gemm.hip", "gemm_tiled.hip", "dma_tile.h", "common.h", "kernels.h"],
+    "lmhead_topk": ["gemm.hip", "lmhead_tiled.hip", "dma_tile.h", "common.h", "kernels.h"],
     "attention": ["attention.hip", "common.h", "kernels.h"],
 }
 
