@@ -478,10 +478,13 @@ struct LmPlan {
   int bm, nM, nN, runs, tpb;
 };
 
-// Row tile (256 or 128 rows) and vocabulary runs: one block per CU (256
-// resident blocks), each sweeping tpb tiles; the choice minimises tpb times
-// the relative cost of a tile (a 128-row tile measured 0.6 of a 256-row one).
-// DFLASH2_LMHEAD_TILES_PER_BLOCK (1..64) overrides tpb.
+// Row tile (256, 192 or 128 rows) and vocabulary runs: one block per CU
+// (256 resident blocks), each sweeping tpb tiles; the choice minimises tpb
+// times the relative cost of a tile (a 128-row tile measured 0.6 of a
+// 256-row one; a 192-row tile is taken as 0.78).  192-row tiles cover 384
+// rows without padding, where 256-row tiles would compute 512.
+// DFLASH2_LMHEAD_TILES_PER_BLOCK (1..64) overrides tpb, DFLASH2_LMHEAD_BM
+// (128, 192 or 256) the row tile.
 LmPlan lm_plan(int M, int V) {
   LmPlan best{};
   double best_cost = 1e300;
@@ -490,7 +493,13 @@ LmPlan lm_plan(int M, int V) {
     const int v = std::atoi(env);
     if (v >= 1 && v <= 64) force = v;
   }
-  for (int bm : {256, 128}) {
+  int force_bm = 0;
+  if (const char* env = std::getenv("DFLASH2_LMHEAD_BM")) {
+    const int v = std::atoi(env);
+    if (v == 128 || v == 192 || v == 256) force_bm = v;
+  }
+  for (int bm : {256, 192, 128}) {
+    if (force_bm && bm != force_bm) continue;
     LmPlan pl;
     pl.bm = bm;
     pl.nM = (M + bm - 1) / bm;
@@ -499,7 +508,7 @@ LmPlan lm_plan(int M, int V) {
     pl.tpb = force ? std::min(force, pl.nN) : (pl.nN + runs_max - 1) / runs_max;
     pl.runs = (pl.nN + pl.tpb - 1) / pl.tpb;
     const double waves = double((int64_t(pl.nM) * pl.runs + 255) / 256);
-    const double cost = waves * pl.tpb * (bm == 256 ? 1.0 : 0.6);
+    const double cost = waves * pl.tpb * (bm == 256 ? 1.0 : (bm == 192 ? 0.78 : 0.6));
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = pl;
@@ -519,9 +528,10 @@ template <typename TW>
 static void launch_lm_t(const LmTiledArgs& a, int bm, hipStream_t s) {
   const int blocks = a.nM * a.runs;
   const dim3 grid(unsigned((blocks + 7) / 8 * 8));
-  // three stage buffers where they fit in LDS (not bf16 with 256 rows)
+  // three stage buffers where they fit in LDS (not bf16 with 256 or 192 rows)
   constexpr int R256 = sizeof(TW) == 1 ? 3 : 2;
   if (bm == 256) hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 256, R256>), grid, dim3(256), 0, s, a);
+  else if (bm == 192) hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 192, R256>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((lmhead_tiled_kernel<TW, 128, 3>), grid, dim3(256), 0, s, a);
 }
 

@@ -302,6 +302,23 @@ def test_lmhead_vocabulary_sweeps(name, monkeypatch):
 
 
 @pytest.mark.parametrize("name", ["medium_bf16", "medium_fp8"])
+@pytest.mark.parametrize("bm", ["192", "256"])
+def test_lmhead_row_tiles(name, bm, monkeypatch):
+    """The tiled lm_head on 192- and 256-row tiles (one ragged tile, or a
+    full and a ragged one), three vocabulary tiles per block: same checks
+    as the default 128-row tiles."""
+    monkeypatch.setenv("DFLASH2_LMHEAD_BM", bm)
+    monkeypatch.setenv("DFLASH2_LMHEAD_TILES_PER_BLOCK", "3")
+    w = synth.get(name)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("name", ["medium_bf16", "medium_fp8"])
 def test_draft_tiled_single_split(name, monkeypatch):
     """Tiled GEMMs with one K split, so gate/up and QKV apply SwiGLU and the
     RoPE / cache stores in their own epilogue: same checks as the default."""
