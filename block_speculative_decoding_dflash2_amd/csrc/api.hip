@@ -188,7 +188,12 @@ AttnPlan plan_attn(const dflash2_config& c, int B) {
   const int kt = attn_sub_chunk(c.weight_dtype == DFLASH2_FP32, c.head_dim);
   const int64_t subs = cdiv(c.max_context, kt);
   const int64_t heads = int64_t(B) * c.num_kv_heads * a.qgroups;
-  const int64_t per_block = std::max<int64_t>(1, cdiv(heads * subs, kTargetBlocks));
+  int64_t target = kTargetBlocks;
+  if (const char* env = std::getenv("DFLASH2_ATTN_TARGET_BLOCKS")) {
+    const int v = std::atoi(env);
+    if (v >= 64 && v <= 65536) target = v;
+  }
+  const int64_t per_block = std::max<int64_t>(1, cdiv(heads * subs, target));
   a.chunk = int(per_block * kt);
   a.nchunks = int(cdiv(c.max_context, a.chunk));
   return a;
