@@ -174,19 +174,35 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
     // lane (r, h) of wave (wv, wm): value 4 q + e of acc[i][j] is vocabulary id
     // n0 + lb + 32 i + 8 q + e, lb = 128 wv + 4 h, of local row WM wm + 32 j + r.
     // Per-lane values are recomputed per tile (see DmaTile::run).
+    auto voff = [](int k) { return 32 * (k >> 4) + 8 * ((k & 15) >> 2) + (k & 3); };
     int lb = 128 * wv + 4 * h;
     asm volatile("" : "+v"(lb));
     const int nvalid = p.N - n0 - lb;   // ids at offsets < nvalid exist
-    __syncthreads();  // every wave's loads have landed and the stage buffers are free
-    // the run's list so far of row tid (requested now, used after the
-    // appends below, so the load latency is hidden)
-    uint64_t G[16];
-    {
-      const int m = m0 + tid;
-      const bool cont = !fresh && tid < BM && m < Mact;
-      const uint64_t* o = p.cand + (int64_t(min(m, p.M - 1)) * p.runs + rg) * 16;
+    // bit k of vmask[hf]: the id of value k of half hf exists (all bits set
+    // but in a ragged last tile)
+    const bool ragged = n0 + kLBN > p.N;
+    uint32_t vmask[2] = {~0u, ~0u};
+    if (ragged) {
+      vmask[0] = vmask[1] = 0u;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) G[q] = cont ? o[q] : 0ull;
+      for (int k = 0; k < 32; ++k) {
+        vmask[0] |= uint32_t(voff(k) < nvalid) << k;
+        vmask[1] |= uint32_t(64 + voff(k) < nvalid) << k;
+      }
+    }
+    __syncthreads();  // every wave's loads have landed and the stage buffers are free
+    // The run's list so far of row tid goes straight into LDS now (no
+    // registers held across the appends below) and is read by the same lane
+    // in the merge: 128 bytes per row, chunk q of the row of lane l of wave
+    // w at glist + 8192 w + 1024 q + 16 l, in the upper halves of the bf16
+    // weight stage buffers or the third activation stage buffer (fp8).
+    static_assert(sizeof(TW) == 2 ? T::WBYTES >= 32768 : (R == 3 && T::XBYTES >= BM * 128),
+                  "the lists fit beside the staging area");
+    char* glist = sizeof(TW) == 2 ? (wave < 2 ? w0 : w1) + 16384 + (wave & 1) * 8192 : x2 + wave * 8192;
+    if (!fresh && 64 * wave < BM) {
+      const uint64_t* o = p.cand + (int64_t(min(m0 + tid, p.M - 1)) * p.runs + rg) * 16;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lds_load16(o + 2 * q, glist + 1024 * q);
     }
 
     // Logits of the lane's 32 values of row j, half hf (vocabulary offsets
@@ -194,16 +210,17 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
     // switch on (j, hf), so that a single copy of the code below, in loops
     // that are not unrolled, serves every row: unrolled per row it would not
     // fit the instruction cache.
-    auto voff = [](int k) { return 32 * (k >> 4) + 8 * ((k & 15) >> 2) + (k & 3); };
     auto logits_half = [&](int jh, float (&x)[32]) {
       const int j = jh >> 1, hf = jh & 1;
       const float iv = inv[WM * wm + 32 * j + r];
       float sv[32];
+      if constexpr (sizeof(TW) == 1) {
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const f32x4 v4 = vscale4[(lb + 64 * hf + voff(4 * g)) >> 2];
+        for (int g = 0; g < 8; ++g) {
+          const f32x4 v4 = vscale4[(lb + 64 * hf + voff(4 * g)) >> 2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[4 * g + e] = v4[e];
+          for (int e = 0; e < 4; ++e) sv[4 * g + e] = v4[e];
+        }
       }
       auto take = [&](auto J, auto HF) {
         constexpr int jj = decltype(J)::value, hh = decltype(HF)::value;
@@ -212,6 +229,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
           for (int k = 0; k < 32; ++k) x[k] = acc[2 * hh + (k >> 4)][jj][k & 15];
         }
       };
+      if (jh >= 2 * FJ) __builtin_unreachable();
       switch (jh) {
         case 0: take(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}); break;
         case 1: take(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}); break;
@@ -225,7 +243,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
         float y = x[k];
-        y *= sv[k];
+        if constexpr (sizeof(TW) == 1) y *= sv[k];   // (bf16 weights have no scales)
         y *= iv;
         x[k] = y + 0.0f;
       }
@@ -267,7 +285,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
           float a = -INFINITY, b = -INFINITY;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const float y = 64 * (jh & 1) + voff(16 * ii + v) < nvalid ? x[16 * ii + v] : -INFINITY;
+            const float y = (vmask[jh & 1] >> (16 * ii + v)) & 1u ? x[16 * ii + v] : -INFINITY;
             b = fmaxf(b, fminf(a, y));
             a = fmaxf(a, y);
           }
@@ -308,6 +326,9 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
     static_assert(WM * NSLOT * 8 <= T::XBYTES, "slots fit an activation stage buffer");
     float* stg = reinterpret_cast<float*>(wave < 2 ? w0 : w1) + (wave & 1) * 32 * WAVE;  // [32][64] per wave
     static_assert(2 * 32 * WAVE * 4 <= T::WBYTES, "staging fits a weight stage buffer");
+    // Slot q of row lm sits at position q ^ (lm % 32) of the row's 32: rows
+    // are 256 bytes apart, so without the swizzle the 32 rows of a wave's
+    // lanes would all hit the same LDS banks.
     auto slots_of = [&](int lm) {
       return reinterpret_cast<uint64_t*>(lm < WM ? x0 : x1) + (lm % WM) * NSLOT;
     };
@@ -345,19 +366,32 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
       logits_half(jh, x);
       uint32_t mk = 0u;
 #pragma unroll
-      for (int k = 0; k < 32; ++k)
-        mk |= (uint32_t(x[k] >= te) & uint32_t(64 * (jh & 1) + voff(k) < nvalid)) << k;
+      for (int k = 0; k < 32; ++k) mk |= uint32_t(x[k] >= te) << k;
+      mk &= vmask[jh & 1];
       if (mk != 0u) {
-        // stage the 32 values (lane-major, wave-private) and visit the set bits
+        // stage the 32 values (lane-major, wave-private) and visit the set
+        // bits, four per round, so that their LDS reads overlap
 #pragma unroll
         for (int k = 0; k < 32; ++k) stg[k * WAVE + lane] = x[k];
         uint64_t* sl = slots_of(lm);
         int pos = atomicAdd(&cnt[lm], __builtin_popcount(mk));
         while (mk != 0u) {
-          const int k = __builtin_ctz(mk);
-          mk &= mk - 1u;
-          if (pos < NSLOT) sl[pos] = rank_key(stg[k * WAVE + lane], uint32_t(n0 + base + voff(k)));
-          ++pos;
+          int kk[4];
+          uint32_t live = 0u;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            kk[u] = mk != 0u ? __builtin_ctz(mk) : 0;
+            live |= uint32_t(mk != 0u) << u;
+            mk &= mk - 1u;
+          }
+          float v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = stg[kk[u] * WAVE + lane];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (((live >> u) & 1u) && pos < NSLOT) sl[pos ^ r] = rank_key(v[u], uint32_t(n0 + base + voff(kk[u])));
+            pos += int((live >> u) & 1u);
+          }
         }
       }
     }
@@ -371,10 +405,23 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
           // (a sorting network and a half-cleaner cascade: short dependency
           // chains, unlike one insertion per key)
           const uint64_t* sl = slots_of(lm);
+          uint64_t G[16];
+          if (fresh) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) G[q] = 0ull;
+          } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // this lane's list has landed in LDS
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const u32x4 v = *reinterpret_cast<const u32x4*>(glist + 1024 * q + 16 * lane);
+              G[2 * q] = uint64_t(v[0]) | (uint64_t(v[1]) << 32);
+              G[2 * q + 1] = uint64_t(v[2]) | (uint64_t(v[3]) << 32);
+            }
+          }
           for (int q0 = 0; q0 < c; q0 += 16) {
             uint64_t Nk[16];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) Nk[q] = q0 + q < c ? sl[q0 + q] : 0ull;
+            for (int q = 0; q < 16; ++q) Nk[q] = q0 + q < c ? sl[(q0 + q) ^ (lm & 31)] : 0ull;
             sort16_keys_desc(Nk);
             uint64_t rev[16];
 #pragma unroll
