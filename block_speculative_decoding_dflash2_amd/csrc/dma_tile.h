@@ -38,6 +38,32 @@ __device__ __forceinline__ void lds_load16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
 }
 
+// The same through a buffer resource: 16 bytes per lane at byte offset
+// voff + soff of the resource's base (soff wave-uniform).
+__device__ __forceinline__ void lds_load16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, voff, soff, 0, 0);
+}
+
+// raw buffer resource over [base, base + 4 GiB) (gfx9 data-format word)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(0xFFFFFFFFu), 0x00020000);
+}
+
+// A wave-uniform value kept in scalar registers (the caller guarantees that
+// every lane holds the same value; the compiler cannot always prove it, and
+// a buffer resource or scalar offset it takes for divergent is loaded in a
+// loop over the lanes' distinct values).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+}
+
+#ifndef DFLASH2_DMA_BUFFER_LOADS
+#define DFLASH2_DMA_BUFFER_LOADS 1
+#endif
+
 // 16-byte chunk permutation of an LDS row
 __device__ __forceinline__ int chunk_perm(int r) { return r ^ (r >> 2); }
 
@@ -105,11 +131,21 @@ struct DmaTile {
     // go out in NPART parts of PQ
     constexpr int NL = WLD + XLD, NPART = NP, PQ = (NL + NPART - 1) / NPART;
     static_assert(NPART >= 1 && NPART <= 4, "a stage's loads go out in one to four parts");
+    // Buffer loads: the wave-uniform stage offset goes in a scalar register
+    // and each lane's offset stays fixed, so a load needs no address
+    // arithmetic on the lanes.
+    const __amdgpu_buffer_rsrc_t wrs = raw_rsrc(uniform_ptr(wbase)), xrs = raw_rsrc(uniform_ptr(xbase));
     auto load_part = [&](int kt, char* wd, char* xd, int part) {
 #pragma unroll
       for (int q = part * PQ; q < (part + 1) * PQ && q < NL; ++q) {
-        if (q < WLD) lds_load16(wbase + woff[q] + uint32_t(kt * WROW), wd + 1024 * (wave * WLD + q));
-        else lds_load16(xbase + xoff[q - WLD] + uint32_t(kt * XROW), xd + 1024 * (wave * XLD + q - WLD));
+        if (DFLASH2_DMA_BUFFER_LOADS) {
+          const uint32_t kts = __builtin_amdgcn_readfirstlane(kt);
+          if (q < WLD) lds_load16_buf(wrs, woff[q], kts * WROW, wd + 1024 * (wave * WLD + q));
+          else lds_load16_buf(xrs, xoff[q - WLD], kts * XROW, xd + 1024 * (wave * XLD + q - WLD));
+        } else {
+          if (q < WLD) lds_load16(wbase + woff[q] + uint32_t(kt * WROW), wd + 1024 * (wave * WLD + q));
+          else lds_load16(xbase + xoff[q - WLD] + uint32_t(kt * XROW), xd + 1024 * (wave * XLD + q - WLD));
+        }
       }
     };
     auto load_stage = [&](int kt, char* wd, char* xd) {
