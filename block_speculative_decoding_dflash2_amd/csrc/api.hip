@@ -639,7 +639,7 @@ static dflash2_status draft_impl(dflash2_handle* handle, hipStream_t stream, int
   ma.cand = la.cand; ma.M = P.Mh; ma.k = c.selector_top_k;
   if (lmhead_tiled_ok(dt, P.Mh, H, c.selector_top_k)) {
     ma.glen = 16;
-    ma.count = lmhead_tiled_lists(P.Mh, c.vocab) * 16;
+    ma.count = lmhead_tiled_lists(dt, P.Mh, c.vocab) * 16;
     ma.lstride = 16; ma.kstride = 1;
   } else {
     ma.glen = c.selector_top_k;

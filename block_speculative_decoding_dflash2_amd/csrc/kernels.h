@@ -200,7 +200,7 @@ constexpr int kTiledMinRows = 64;
 int gemm_rows_per_block(int weight_dtype, int M);
 bool gemm_tiled_ok(int weight_dtype, int M, int K);
 bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k);
-int lmhead_tiled_lists(int M, int V);
+int lmhead_tiled_lists(int weight_dtype, int M, int V);
 // Block tile of the LDS-tiled GEMM: bm activation rows x 256 weight rows,
 // per_cu blocks resident per CU.  bm = the requested 256 or 128 (0: the
 // default for M rows); DFLASH2_TILED_BM overrides it.

@@ -244,8 +244,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
       for (int k = 0; k < 32; ++k) {
         float y = x[k];
         if constexpr (sizeof(TW) == 1) y *= sv[k];   // (bf16 weights have no scales)
-        y *= iv;
-        x[k] = y + 0.0f;
+        x[k] = y * iv;   // (-0.0 is ranked as +0.0 by the key)
       }
     };
     static_assert(FJ <= 4, "at most four row blocks per wave");
@@ -527,12 +526,14 @@ struct LmPlan {
 
 // Row tile (256, 192 or 128 rows) and vocabulary runs: one block per CU
 // (256 resident blocks), each sweeping tpb tiles; the choice minimises tpb
-// times the relative cost of a tile (a 128-row tile measured 0.6 of a
-// 256-row one; a 192-row tile is taken as 0.78).  192-row tiles cover 384
+// times the relative cost of a tile against a 256-row one: 128-row tiles
+// 0.6 (fp8) or 0.55 (bf16, whose 256-row tiles fit only two stage buffers
+// in LDS and wait longer on the weight stream: measured 384 against 428 us
+// at 240 x 151936 x 4096), 192-row tiles 0.78.  192-row tiles cover 384
 // rows without padding, where 256-row tiles would compute 512.
 // DFLASH2_LMHEAD_TILES_PER_BLOCK (1..64) overrides tpb, DFLASH2_LMHEAD_BM
 // (128, 192 or 256) the row tile.
-LmPlan lm_plan(int M, int V) {
+LmPlan lm_plan(int weight_dtype, int M, int V) {
   LmPlan best{};
   double best_cost = 1e300;
   int force = 0;
@@ -555,7 +556,8 @@ LmPlan lm_plan(int M, int V) {
     pl.tpb = force ? std::min(force, pl.nN) : (pl.nN + runs_max - 1) / runs_max;
     pl.runs = (pl.nN + pl.tpb - 1) / pl.tpb;
     const double waves = double((int64_t(pl.nM) * pl.runs + 255) / 256);
-    const double cost = waves * pl.tpb * (bm == 256 ? 1.0 : (bm == 192 ? 0.78 : 0.6));
+    const double rel128 = weight_dtype == 1 ? 0.55 : 0.6;
+    const double cost = waves * pl.tpb * (bm == 256 ? 1.0 : (bm == 192 ? 0.78 : rel128));
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = pl;
@@ -569,7 +571,7 @@ bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k) {
   return weight_dtype != 0 && M > kTiledMinRows && K % kLKT == 0 && k <= 16;
 }
 
-int lmhead_tiled_lists(int M, int V) { return lm_plan(M, V).runs; }
+int lmhead_tiled_lists(int weight_dtype, int M, int V) { return lm_plan(weight_dtype, M, V).runs; }
 
 template <typename TW>
 static void launch_lm_t(const LmTiledArgs& a, int bm, hipStream_t s) {
@@ -583,7 +585,7 @@ static void launch_lm_t(const LmTiledArgs& a, int bm, hipStream_t s) {
 }
 
 void launch_lmhead_tiled(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
-  const LmPlan pl = lm_plan(a.M, a.N);
+  const LmPlan pl = lm_plan(weight_dtype, a.M, a.N);
   LmTiledArgs t{};
   t.X = static_cast<const bf16_t*>(a.X); t.ldx = a.ldx;
   t.W = a.W; t.ldw = a.ldw; t.scale = a.scale;
