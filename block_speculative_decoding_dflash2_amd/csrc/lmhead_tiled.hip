@@ -210,10 +210,8 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
     // switch on (j, hf), so that a single copy of the code below, in loops
     // that are not unrolled, serves every row: unrolled per row it would not
     // fit the instruction cache.
-    auto logits_half = [&](int jh, float (&x)[32]) {
-      const int j = jh >> 1, hf = jh & 1;
-      const float iv = inv[WM * wm + 32 * j + r];
-      float sv[32];
+    // (sv: the per-vocabulary-row scales of half hf, fp8 weights only)
+    auto load_sv = [&](int hf, float (&sv)[32]) {
       if constexpr (sizeof(TW) == 1) {
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
@@ -222,6 +220,10 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
           for (int e = 0; e < 4; ++e) sv[4 * g + e] = v4[e];
         }
       }
+    };
+    auto logits_half_sv = [&](int jh, float (&x)[32], const float (&sv)[32]) {
+      const int j = jh >> 1;
+      const float iv = inv[WM * wm + 32 * j + r];
       auto take = [&](auto J, auto HF) {
         constexpr int jj = decltype(J)::value, hh = decltype(HF)::value;
         if constexpr (jj < FJ) {
@@ -246,6 +248,11 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
         if constexpr (sizeof(TW) == 1) y *= sv[k];   // (bf16 weights have no scales)
         x[k] = y * iv;   // (-0.0 is ranked as +0.0 by the key)
       }
+    };
+    auto logits_half = [&](int jh, float (&x)[32]) {
+      float sv[32];
+      load_sv(jh & 1, sv);
+      logits_half_sv(jh, x, sv);
     };
     static_assert(FJ <= 4, "at most four row blocks per wave");
     // bit k: value x[k] can enter the row's list (ids past the vocabulary
@@ -355,14 +362,19 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
         }
       }
     }
+    // (fp8: half-major, so that a half's scales are read once)
+    float sv[32];
 #pragma nounroll
-    for (int jh = 0; jh < 2 * FJ; ++jh) {
-      const int lm = WM * wm + 32 * (jh >> 1) + r;
-      const int base = lb + 64 * (jh & 1);   // vocabulary offset of x[0] in the tile
+    for (int it = 0; it < 2 * FJ; ++it) {
+      const int j = sizeof(TW) == 1 ? it % FJ : it >> 1, hf = sizeof(TW) == 1 ? it / FJ : it & 1;
+      if (j == 0) load_sv(hf, sv);
+      const int jh = 2 * j + hf;
+      const int lm = WM * wm + 32 * j + r;
+      const int base = lb + 64 * hf;   // vocabulary offset of x[0] in the tile
       const uint64_t tk = thrk[lm];
       const float te = fresh ? thr[lm] : (tk == 0ull ? -__FLT_MAX__ : key_val(tk));
       float x[32];
-      logits_half(jh, x);
+      logits_half_sv(jh, x, sv);
       uint32_t mk = 0u;
 #pragma unroll
       for (int k = 0; k < 32; ++k) mk |= uint32_t(x[k] >= te) << k;
