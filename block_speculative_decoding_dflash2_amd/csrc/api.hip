@@ -98,8 +98,9 @@ Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
     // resident tiles (256 CUs x tiles per CU), each costing its k range plus
     // a fixed prologue/epilogue of about 512 k at ~1.2 PF/s of 256-row tiles
     // (fp8 128-row tiles, two per CU, measured up to ~10% slower per flop
-    // than 256-row tiles with three stage buffers; bf16 128-row tiles, one
-    // per CU, ~20% slower), plus the float32 partial
+    // than 256-row tiles with three stage buffers, fp8 192-row tiles taken
+    // as 4% slower; bf16 128-row tiles, one per CU, ~20% slower), plus the
+    // float32 partial
     // sums every split writes and its consumer reads back (8 bytes per
     // output per split at ~5 TB/s); ties go to fewer splits and larger
     // tiles, at most 8 splits.
@@ -109,12 +110,12 @@ Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
       if (v >= 1 && v <= 16) max_splits = v;
     }
     double best_cost = 1e300;
-    for (int bm : {256, 128}) {
+    for (int bm : {256, 192, 128}) {
       const TiledShape sh = tiled_shape(dtype, M, bm);
       if (sh.bm != bm) continue;
       const int64_t tiles = cdiv(M, sh.bm) * cdiv(N, 256) * groups;
       const int64_t slots = 256 * int64_t(sh.per_cu);
-      const double eff = sh.bm == 256 ? 1.0 : (sh.per_cu == 2 ? 1.1 : 1.2);
+      const double eff = sh.bm == 256 ? 1.0 : (sh.bm == 192 ? 1.04 : (sh.per_cu == 2 ? 1.1 : 1.2));
       const double us_per_k = 2.0 * 256.0 * sh.bm * sh.per_cu / 4.7e6 * eff;  // one tile, per k, in us
       for (int S = 1; S <= max_splits; ++S) {
         const int64_t ks = cdiv(cdiv(K, S), 64) * 64;

@@ -7,6 +7,9 @@
 // rows per block, both operands loaded straight into LDS).  Tile shapes:
 //  * BM = 256, one block per CU (256 accumulators per lane), three stage
 //    buffers for fp8 weights and two for bf16 (LDS);
+//  * BM = 192 (fp8 weights): one block per CU, three stage buffers; a row
+//    count that is a multiple of 192 but not of 256, or a tile count just
+//    above a multiple of 256, wastes less;
 //  * BM = 128 for at most 128 rows: fp8 two blocks per CU with two stage
 //    buffers each, bf16 one block with three.
 // Tiles are numbered with the activation tile fastest and dealt out so that
@@ -278,10 +281,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 // host side
 // ---------------------------------------------------------------------------
 TiledShape tiled_shape(int weight_dtype, int M, int bm) {
-  if (bm != 128 && bm != 256) bm = M > 128 ? 256 : 128;
+  if (bm != 128 && bm != 256 && !(bm == 192 && weight_dtype == 2)) bm = M > 128 ? 256 : 128;
   if (const char* env = std::getenv("DFLASH2_TILED_BM")) {
     const int v = std::atoi(env);
-    if (v == 128 || v == 256) bm = v;
+    if (v == 128 || v == 256 || (v == 192 && weight_dtype == 2)) bm = v;
   }
   // fp8 128-row tiles: two blocks per CU (two 32 KB stage buffers each)
   return TiledShape{bm, (bm == 128 && weight_dtype == 2) ? 2 : 1};
@@ -329,6 +332,7 @@ void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s) {
     else launch_tiled_t<bf16_t, 128, 3, 1>(t, s);
   } else {
     if (sh.bm == 256) launch_tiled_t<fp8_t, 256, 3, 1>(t, s);
+    else if (sh.bm == 192) launch_tiled_t<fp8_t, 192, 3, 1>(t, s);
     else launch_tiled_t<fp8_t, 128, 2, 2>(t, s);
   }
 }

@@ -202,8 +202,8 @@ bool gemm_tiled_ok(int weight_dtype, int M, int K);
 bool lmhead_tiled_ok(int weight_dtype, int M, int K, int k);
 int lmhead_tiled_lists(int weight_dtype, int M, int V);
 // Block tile of the LDS-tiled GEMM: bm activation rows x 256 weight rows,
-// per_cu blocks resident per CU.  bm = the requested 256 or 128 (0: the
-// default for M rows); DFLASH2_TILED_BM overrides it.
+// per_cu blocks resident per CU.  bm = the requested 256, 192 (fp8 weights
+// only) or 128 (0: the default for M rows); DFLASH2_TILED_BM overrides it.
 struct TiledShape { int bm, per_cu; };
 TiledShape tiled_shape(int weight_dtype, int M, int bm);
 void launch_gemm_tiled(int weight_dtype, const GemmArgs& a, hipStream_t s);

@@ -350,6 +350,22 @@ def test_draft_tiled_128_row_tiles(name, splits, monkeypatch):
         g.close()
 
 
+@pytest.mark.parametrize("splits", ["1", "8"])
+def test_draft_tiled_192_row_tiles(splits, monkeypatch):
+    """fp8 tiled GEMMs on 192-row block tiles (three accumulator row blocks
+    per wave, three stage buffers): 280 rows in a full and a ragged row
+    tile, one K split (SwiGLU and QKV epilogues) and the planner's splits."""
+    monkeypatch.setenv("DFLASH2_TILED_BM", "192")
+    monkeypatch.setenv("DFLASH2_TILED_MAX_SPLITS", splits)
+    w = synth.get("medium_fp8")
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
+
+
 @pytest.mark.parametrize("name,window", [("small_bf16", 64), ("medium_fp8", 100), ("small_fp32", 33),
                                          ("tiny_fp32", 8)])
 def test_draft_sliding_window(name, window):
