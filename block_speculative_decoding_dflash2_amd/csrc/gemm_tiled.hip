@@ -291,7 +291,7 @@ TiledShape tiled_shape(int weight_dtype, int M, int bm) {
 }
 
 bool gemm_tiled_ok(int weight_dtype, int M, int K) {
-  return weight_dtype != 0 && M > kTiledMinRows && K % kDmaKT == 0;
+  return weight_dtype != 0 && M > kTiledMinRowsGemm && K % kDmaKT == 0;
 }
 
 template <typename TW, int BM, int R, int OCC>

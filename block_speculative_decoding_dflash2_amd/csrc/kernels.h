@@ -194,8 +194,14 @@ void launch_loss_seq(const LossArgs& a, hipStream_t s);   // per-sequence sums, 
 // Kept sets of at most this many entries are handed from the row pass to the draw.
 constexpr int SV_OUT = 256;
 
-// Activation rows above which the LDS-tiled, compute-bound GEMMs are used.
+// Activation rows above which the LDS-tiled, compute-bound lm_head is used.
 constexpr int kTiledMinRows = 64;
+// Activation rows above which the linears take the LDS-tiled GEMM: from 33
+// rows the weight-streaming kernel holds four activation fragments per k-step
+// and keeps one load group in flight (its registers are full), and the tiled
+// one streams the weights faster (measured on 60 context rows of the
+// long-block workload: context K/V projection 34.8 -> 23.7 us).
+constexpr int kTiledMinRowsGemm = 32;
 
 int gemm_rows_per_block(int weight_dtype, int M);
 bool gemm_tiled_ok(int weight_dtype, int M, int K);
