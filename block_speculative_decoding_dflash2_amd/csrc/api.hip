@@ -103,8 +103,10 @@ Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
     // float32 partial
     // sums every split writes and its consumer reads back (8 bytes per
     // output per split at ~5 TB/s); ties go to fewer splits and larger
-    // tiles, at most 8 splits.
-    int max_splits = 8;
+    // tiles, at most 16 splits (a 60 x 4096 x 16384 projection of the
+    // long-block workload ran 51 us on 8 splits, 42 us on 16: 16 column tiles
+    // need 16 splits to occupy the 256 CUs).
+    int max_splits = 16;
     if (const char* env = std::getenv("DFLASH2_TILED_MAX_SPLITS")) {
       const int v = std::atoi(env);
       if (v >= 1 && v <= 16) max_splits = v;
