@@ -222,6 +222,13 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
       }
     };
     auto logits_half_sv = [&](int jh, float (&x)[32], const float (&sv)[32]) {
+      // (an empty asm over the accumulators stops the compiler from hoisting
+      // their copies out of the loops that call this, which ran the 192-row
+      // kernel out of registers)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FJ; ++jj) asm volatile("" : "+a"(acc[i][jj]));
       const int j = jh >> 1;
       const float iv = inv[WM * wm + 32 * j + r];
       auto take = [&](auto J, auto HF) {
