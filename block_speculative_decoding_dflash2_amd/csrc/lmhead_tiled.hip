@@ -369,7 +369,15 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
         }
       }
     }
-    // (fp8: half-major, so that a half's scales are read once)
+    // (fp8: half-major, so that a half's scales are read once; the bounds of
+    // the lane's rows are read before the loop, so no LDS wait heads it)
+    float tes[FJ];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int lm = WM * wm + 32 * j + r;
+      const uint64_t tk = thrk[lm];
+      tes[j] = fresh ? thr[lm] : (tk == 0ull ? -__FLT_MAX__ : key_val(tk));
+    }
     float sv[32];
 #pragma nounroll
     for (int it = 0; it < 2 * FJ; ++it) {
@@ -378,8 +386,9 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
       const int jh = 2 * j + hf;
       const int lm = WM * wm + 32 * j + r;
       const int base = lb + 64 * hf;   // vocabulary offset of x[0] in the tile
-      const uint64_t tk = thrk[lm];
-      const float te = fresh ? thr[lm] : (tk == 0ull ? -__FLT_MAX__ : key_val(tk));
+      float te = tes[0];
+#pragma unroll
+      for (int q = 1; q < FJ; ++q) te = j == q ? tes[q] : te;
       float x[32];
       logits_half_sv(jh, x, sv);
       uint32_t mk = 0u;
