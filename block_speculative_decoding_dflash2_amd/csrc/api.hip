@@ -197,7 +197,10 @@ AttnPlan plan_attn(const dflash2_config& c, int B) {
     const int v = std::atoi(env);
     if (v >= 64 && v <= 65536) target = v;
   }
-  const int64_t per_block = std::max<int64_t>(1, cdiv(heads * subs, target));
+  // at least three sub-chunks per block: with fewer (8 heads at batch 1, the
+  // 27B-class workload) the partials and their merge cost more than the
+  // extra blocks gain (attention + merge 101 -> 94 us per step)
+  const int64_t per_block = std::max<int64_t>(std::min<int64_t>(3, subs), cdiv(heads * subs, target));
   a.chunk = int(per_block * kt);
   a.nchunks = int(cdiv(c.max_context, a.chunk));
   return a;

@@ -370,9 +370,10 @@ def test_draft_tiled_192_row_tiles(splits, monkeypatch):
                                          ("tiny_fp32", 8)])
 def test_draft_sliding_window(name, window):
     """draft_sliding_window: attention reaches back `window` context rows;
-    sequences both shorter and longer than the window.  tiny_fp32 plans one
-    key chunk, so the attention kernel writes its output without the merge
-    pass; the others merge several chunks."""
+    sequences both shorter and longer than the window.  tiny_fp32 and
+    small_fp32 plan one key chunk (a block takes at least three 64-key
+    sub-chunks), so the attention kernel writes its output without the merge
+    pass; the bf16 and fp8 cases merge several chunks."""
     w = synth.get(name).replace(sliding_window=window)
     g = DraftRun(w)
     try:
