@@ -1,14 +1,15 @@
 // Main loop shared by the compute-bound GEMMs (the LDS-tiled linears and the
 // lm_head of many activation rows): a block tile of 256 weight rows x BM
-// activation rows (BM = 256 or 128), 4 waves in a 2 x 2 layout; wave
+// activation rows (BM = 256, 192 or 128), 4 waves in a 2 x 2 layout; wave
 // (wv, wm) owns weight rows [128 wv, 128 wv + 128) of the tile against
 // activation rows [BM/2 wm, BM/2 (wm + 1)): 4 x BM/64 tiles of
 // v_mfma_f32_32x32x16_bf16 (up to 256 accumulators, one wave per SIMD).
-// Both operands go from global memory straight into LDS
-// (global_load_lds_dwordx4: 16 bytes per lane, no register round trip), 64 k
-// per stage, with R = 2 or 3 stage buffers (one or two stages of loads in
-// flight); each stage buffer is its own LDS object, so the compiler waits
-// only for the loads of the buffer it reads.  Rows are 128 bytes
+// Both operands go from global memory straight into LDS (buffer loads to
+// LDS: 16 bytes per lane, no register round trip; scalar base and stage
+// offset, a fixed 32-bit offset per lane), 64 k per stage, with R = 2 or 3
+// stage buffers (one or two stages of loads in flight); each stage buffer is
+// its own LDS object, so the compiler waits only for the loads of the buffer
+// it reads.  A stage's loads go out in parts spread over the MFMAs.  Rows are 128 bytes
 // (activations, bf16 weights) or 64 bytes (fp8 weights) with the 16-byte
 // chunks of row r XOR-permuted by (r ^ (r >> 2)): the 32 x 32 x 16 operand
 // reads (row = lane % 32, chunk by lane / 32) then hit distinct banks
@@ -59,10 +60,6 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
   return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
 }
-
-#ifndef DFLASH2_DMA_BUFFER_LOADS
-#define DFLASH2_DMA_BUFFER_LOADS 1
-#endif
 
 // 16-byte chunk permutation of an LDS row
 __device__ __forceinline__ int chunk_perm(int r) { return r ^ (r >> 2); }
@@ -138,14 +135,9 @@ struct DmaTile {
     auto load_part = [&](int kt, char* wd, char* xd, int part) {
 #pragma unroll
       for (int q = part * PQ; q < (part + 1) * PQ && q < NL; ++q) {
-        if (DFLASH2_DMA_BUFFER_LOADS) {
-          const uint32_t kts = __builtin_amdgcn_readfirstlane(kt);
-          if (q < WLD) lds_load16_buf(wrs, woff[q], kts * WROW, wd + 1024 * (wave * WLD + q));
-          else lds_load16_buf(xrs, xoff[q - WLD], kts * XROW, xd + 1024 * (wave * XLD + q - WLD));
-        } else {
-          if (q < WLD) lds_load16(wbase + woff[q] + uint32_t(kt * WROW), wd + 1024 * (wave * WLD + q));
-          else lds_load16(xbase + xoff[q - WLD] + uint32_t(kt * XROW), xd + 1024 * (wave * XLD + q - WLD));
-        }
+        const uint32_t kts = __builtin_amdgcn_readfirstlane(kt);
+        if (q < WLD) lds_load16_buf(wrs, woff[q], kts * WROW, wd + 1024 * (wave * WLD + q));
+        else lds_load16_buf(xrs, xoff[q - WLD], kts * XROW, xd + 1024 * (wave * XLD + q - WLD));
       }
     };
     auto load_stage = [&](int kt, char* wd, char* xd) {
