@@ -350,6 +350,22 @@ def test_draft_tiled_128_row_tiles(name, splits, monkeypatch):
         g.close()
 
 
+@pytest.mark.parametrize("name,batch", [("small_bf16", 5), ("small_bf16", 8), ("small_fp8", 9)])
+def test_draft_tiled_few_rows(name, batch):
+    """33-64 activation rows: the linears whose depth is a multiple of 64 take
+    the LDS-tiled GEMM (one ragged row tile, split K; the FFN down projection
+    of depth 736 stays on the weight-streaming kernel), the lm_head (at most
+    64 rows) the weight-streaming kernel."""
+    w = synth.get(name).replace(batch=batch)
+    assert 32 < w.batch * w.block_size <= 64 or 32 < w.batch * (w.block_size - 1) <= 64
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
+
+
 @pytest.mark.parametrize("splits", ["1", "8"])
 def test_draft_tiled_192_row_tiles(splits, monkeypatch):
     """fp8 tiled GEMMs on 192-row block tiles (three accumulator row blocks
