@@ -206,4 +206,21 @@ __device__ __forceinline__ void bitonic_top(uint64_t (&a)[KMAX], const uint64_t 
 
 __device__ __forceinline__ float key_val(uint64_t k) { return unordered_f32(uint32_t(k >> 32)); }
 
+// Sum of p[0..n) added in index order, with the loads of 32 consecutive
+// values issued together (one memory round trip per 32 values rather than
+// one per value).  Used for an activation row's per-column-block sums of
+// squares, from which a GEMM applies the row's RMSNorm factor.
+__device__ __forceinline__ float sum_in_order(const float* __restrict__ p, int n) {
+  float s = 0.f;
+  for (int c = 0; c < n; c += 32) {
+    float v[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) v[e] = p[min(c + e, n - 1)];
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if (c + e < n) s += v[e];
+  }
+  return s;
+}
+
 }  // namespace dfl

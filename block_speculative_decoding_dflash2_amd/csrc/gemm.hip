@@ -155,8 +155,7 @@ struct GemmTile {
 // to the GEMM result because it is one factor per row.
 __device__ __forceinline__ float row_inv_rms(const RowScale& rs, int m) {
   if (!rs.sumsq) return 1.f;
-  float s = 0.f;
-  for (int c = 0; c < rs.blocks; ++c) s += rs.sumsq[int64_t(m) * rs.blocks + c];
+  const float s = sum_in_order(rs.sumsq + int64_t(m) * rs.blocks, rs.blocks);
   return 1.0f / sqrtf(s * rs.inv_width + rs.eps);
 }
 

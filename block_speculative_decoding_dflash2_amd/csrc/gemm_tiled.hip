@@ -103,8 +103,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     float v = 1.f;
     const int m = m0 + t;
     if (p.rs.sumsq && m < Mact) {
-      float s = 0.f;
-      for (int c = 0; c < p.rs.blocks; ++c) s += p.rs.sumsq[int64_t(m) * p.rs.blocks + c];
+      const float s = sum_in_order(p.rs.sumsq + int64_t(m) * p.rs.blocks, p.rs.blocks);
       v = 1.0f / sqrtf(s * p.rs.inv_width + p.rs.eps);
     }
     inv[t] = v;

@@ -140,8 +140,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(LmTiledArgs p) {
     float v = 1.f;
     const int m = m0 + q;
     if (p.rs.sumsq && m < Mact) {
-      float s = 0.f;
-      for (int c = 0; c < p.rs.blocks; ++c) s += p.rs.sumsq[int64_t(m) * p.rs.blocks + c];
+      const float s = sum_in_order(p.rs.sumsq + int64_t(m) * p.rs.blocks, p.rs.blocks);
       v = 1.0f / sqrtf(s * p.rs.inv_width + p.rs.eps);
     }
     inv[q] = v;
