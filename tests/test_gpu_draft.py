@@ -366,6 +366,21 @@ def test_draft_tiled_few_rows(name, batch):
         g.close()
 
 
+@pytest.mark.parametrize("name,batch", [("small_bf16", 1), ("small_bf16", 2), ("small_fp8", 1), ("small_fp8", 2)])
+def test_draft_streaming_few_rows(name, batch):
+    """At most 16 activation rows (7-16 here): the weight-streaming GEMMs copy
+    each block's rows of the activations into LDS and read their operands
+    from there; the lm_head streams its weights too."""
+    w = synth.get(name).replace(batch=batch)
+    assert w.batch * w.block_size <= 16
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
+
+
 @pytest.mark.parametrize("splits", ["1", "8"])
 def test_draft_tiled_192_row_tiles(splits, monkeypatch):
     """fp8 tiled GEMMs on 192-row block tiles (three accumulator row blocks
