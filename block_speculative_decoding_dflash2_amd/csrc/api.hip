@@ -212,7 +212,7 @@ struct Plan {
   AttnPlan attn;
   int groups;
   size_t off_h0, off_h1, off_n, off_sumsq, off_q, off_o, off_a, off_parts, off_attn_o, off_attn_ml,
-      off_cand, off_hpre;
+      off_cand, off_cand2, off_hpre;
   size_t total;
 };
 
@@ -266,6 +266,8 @@ Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
   // candidate lists: the weight-streaming lm_head writes groups x k keys per
   // row, the tiled one at most groups lists of 16
   p.off_cand = take(size_t(p.Mh) * p.groups * std::max(c.selector_top_k, 16) * 8);
+  // their first fold (k <= 16, more than 64 lists per row): 16 keys per 64 lists
+  p.off_cand2 = take(size_t(p.Mh) * topk_premerge_lists(p.groups) * 16 * 8);
   // dynamic convolution: each conv site's input rows, float32
   p.off_hpre = gk > 0 ? take(size_t(p.M) * H * 4) : 0;
   p.total = off;
@@ -654,12 +656,25 @@ static dflash2_status draft_impl(dflash2_handle* handle, hipStream_t stream, int
   }
   ma.M_dev = nullptr; ma.ids = topk_ids; ma.vals = topk_vals;
   ma.multiplier = c.output_multiplier; ma.softcap = c.final_logit_softcapping;
+  if (c.selector_top_k <= 16 && ma.count / ma.glen > 256) {
+    // more than 256 lists per row (more than one per thread of the merge
+    // kernel's block): fold them 64 at a time first, with one wave per 64
+    // lists of a row (the weight-streaming lm_head writes one list per 128
+    // ids: 1187 per row at a 151936 vocabulary; at batch 1, merge kernel +
+    // selector 38.5 us per step, fold + merging selector 33.0)
+    uint64_t* c2 = reinterpret_cast<uint64_t*>(ws + P.off_cand2);
+    const int nc = topk_premerge_lists(ma.count / ma.glen);
+    traced(stream, DFLASH2_K_TOPK_MERGE, int64_t(P.Mh) * ma.count * 8 + int64_t(P.Mh) * nc * 16 * 8, 0,
+           [&] { launch_topk_premerge(ma, c2, stream); });
+    ma.cand = c2; ma.count = nc * 16; ma.glen = 16; ma.lstride = 16; ma.kstride = 1;
+  }
   if (path_idx && c.selector_top_k <= 16 && ma.count / ma.glen <= 64) {
     // ---- 4. candidate merge + path selector in one launch: the selector's
-    // kernel merges the (at most 64) sorted lists of each row itself.  With
-    // more lists (the weight-streaming lm_head writes one per 128 ids) the
-    // merge keeps its own kernel: one wave per row cannot fold them as fast
-    // as one block per row does.
+    // kernel merges the (at most 64) sorted lists of each row itself, one
+    // wave per row and a block per sequence.  With 65-256 lists the merge
+    // keeps its own kernel, a block per row (the tiled lm_head's 119-128
+    // runs per row at the long-block and batched workloads: 39.3 / 32.2 us
+    // per step against 45.6 / 33.7 folded and merged in the selector).
     SelectArgs a{};
     a.cand = ma.cand; a.count = ma.count; a.glen = ma.glen; a.lstride = ma.lstride; a.kstride = ma.kstride;
     a.anchors = anchor_ids; a.ids = topk_ids; a.vals = topk_vals;

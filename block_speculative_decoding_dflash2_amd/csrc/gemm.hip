@@ -347,6 +347,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
   }
 }
 
+// First fold of many candidate lists (k <= 16): block (c, m), one wave, merges
+// lists [64 c, 64 c + 64) of row m -- one list per lane, then six xor rounds
+// of the two-list merge below -- into the 16 largest keys, written sorted at
+// out[(m nc + c) 16] (zeros where fewer).  The rows' nc lists then go to the
+// final merge: a row's lists are folded by 64 x the rows' blocks at once
+// instead of by the 256 threads of one block.
+__global__ __launch_bounds__(64) void topk_premerge_kernel(TopkMergeArgs p, uint64_t* out, int nc) {
+  const int Mact = p.M_dev ? min(*p.M_dev, p.M) : p.M;
+  const int m = blockIdx.y;
+  if (m >= Mact) return;
+  const int lane = threadIdx.x;
+  const uint64_t* c = p.cand + int64_t(m) * p.count;
+  const int groups = p.count / p.glen;
+  const int gi = blockIdx.x * WAVE + lane;
+  uint64_t best[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    best[j] = (gi < groups && j < p.glen) ? c[int64_t(gi) * p.lstride + int64_t(j) * p.kstride] : 0ull;
+  for (int d = 1; d < WAVE; d <<= 1) {
+    uint64_t brev[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) brev[j] = __shfl_xor(best[15 - j], d, WAVE);
+    bitonic_top<16>(best, brev);
+  }
+  if (lane < 16) {
+    uint64_t v = best[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) v = lane == j ? best[j] : v;
+    out[(int64_t(m) * nc + blockIdx.x) * 16 + lane] = v;
+  }
+}
+
 // Final top-k over the per-group candidates of one row, then the logit
 // transform.  grid = (M), block = 256.  The lm_head kernels emit sorted
 // lists of glen keys (largest first; glen <= KMAX) and keys are distinct
@@ -518,9 +550,18 @@ void launch_lmhead_topk(int weight_dtype, const LmHeadArgs& a, hipStream_t s) {
 void launch_topk_merge(const TopkMergeArgs& a, hipStream_t s) {
   // (1024 threads per row, one list each, measured slower: 22 vs 19 us at
   // 7 rows, 124 vs 73 us at 1792 rows -- the shuffle rounds dominate)
-  if (a.k <= 16)
+  if (a.k <= 16 && a.count / a.glen <= 64)
+    hipLaunchKernelGGL((topk_merge_kernel<16, 64>), dim3(a.M), dim3(64), 0, s, a);
+  else if (a.k <= 16)
     hipLaunchKernelGGL((topk_merge_kernel<16, 256>), dim3(a.M), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(topk_merge_rounds_kernel, dim3(a.M), dim3(256), 0, s, a);
+}
+
+int topk_premerge_lists(int lists) { return (lists + WAVE - 1) / WAVE; }
+
+void launch_topk_premerge(const TopkMergeArgs& a, uint64_t* out, hipStream_t s) {
+  const int nc = topk_premerge_lists(a.count / a.glen);
+  hipLaunchKernelGGL(topk_premerge_kernel, dim3(nc, a.M), dim3(64), 0, s, a, out, nc);
 }
 
 }  // namespace dfl

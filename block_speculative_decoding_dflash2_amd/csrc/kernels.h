@@ -220,6 +220,11 @@ void launch_gemm(int weight_dtype, const GemmArgs& a, hipStream_t s);
 bool gemm_epi_fusable(int weight_dtype, const GemmArgs& a);
 void launch_lmhead_topk(int weight_dtype, const LmHeadArgs& a, hipStream_t s);
 void launch_topk_merge(const TopkMergeArgs& a, hipStream_t s);
+// Lists per row after the first fold of `lists` lists (k <= 16), and that
+// fold: the 16 best keys of each run of 64 lists, sorted, at
+// out[(m * topk_premerge_lists(lists) + c) * 16].
+int topk_premerge_lists(int lists);
+void launch_topk_premerge(const TopkMergeArgs& a, uint64_t* out, hipStream_t s);
 int norm_col_blocks(int H);
 void launch_norm(bool f32, const NormArgs& a, hipStream_t s);
 void launch_qkv_epilogue(bool f32, const QkvEpiArgs& a, hipStream_t s);

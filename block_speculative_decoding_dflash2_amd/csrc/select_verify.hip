@@ -92,10 +92,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs p, int t
   const int anchor = p.anchors[b];
   if (p.cand) {
     // ---- fused candidate merge (at most 64 sorted lists per row): one wave
-    // per row, lane l holding list l in registers; each of the k rounds
-    // takes the largest head (wave maximum; keys are unique) and the lane
-    // that held it shifts its list by one.  The result is that row's k best
-    // keys, as the separate merge kernel finds them.
+    // per row, lane l holding list l in registers; xor rounds over the lanes
+    // each merge two lanes' lists into the 16 largest keys of both; after the
+    // rounds d < max(lists, 16), lanes 0-15 hold the row's 16 best (keys are
+    // unique), as the separate merge kernel finds them, and lane j < k
+    // writes the j-th.  (The 16 shuffles of a round are independent; k
+    // rounds of a wave maximum each, one shuffle after another, took ~15 us
+    // longer at 7 rows of 19 lists.)
     const int wave = tid / WAVE, lane = tid & (WAVE - 1);
     const int nlists = p.count / p.glen;
     for (int t = wave; t < P; t += kSelThreads / WAVE) {
@@ -104,18 +107,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs p, int t
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         L[j] = (lane < nlists && j < p.glen) ? c[int64_t(lane) * p.lstride + int64_t(j) * p.kstride] : 0ull;
-      for (int j = 0; j < k; ++j) {
-        const uint64_t best = wave_max_u64(L[0]);
-        const bool mine = L[0] == best && best != 0ull;
+      for (int d = 1; d < max(nlists, 16); d <<= 1) {
+        uint64_t brev[16];
 #pragma unroll
-        for (int q = 0; q < 15; ++q) L[q] = mine ? L[q + 1] : L[q];
-        L[15] = mine ? 0ull : L[15];
-        if (lane == 0) {
-          float z = p.multiplier * key_val(best);
-          if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
-          p.ids_out[(int64_t(b) * P + t) * k + j] = int32_t(key_id(best));
-          p.vals_out[(int64_t(b) * P + t) * k + j] = z;
-        }
+        for (int j = 0; j < 16; ++j) brev[j] = __shfl_xor(L[15 - j], d, WAVE);
+        bitonic_top<16>(L, brev);
+      }
+      uint64_t best = L[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) best = lane == j ? L[j] : best;
+      if (lane < k) {
+        float z = p.multiplier * key_val(best);
+        if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
+        p.ids_out[(int64_t(b) * P + t) * k + lane] = int32_t(key_id(best));
+        p.vals_out[(int64_t(b) * P + t) * k + lane] = z;
       }
     }
     __syncthreads();

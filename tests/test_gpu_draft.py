@@ -381,6 +381,26 @@ def test_draft_streaming_few_rows(name, batch):
         g.close()
 
 
+@pytest.mark.parametrize("name,changes,tpb", [
+    ("small_bf16", dict(vocab=40000, top_k=8), None),   # 313 lists of 8 keys per row: folded to 5
+    ("small_fp8", dict(vocab=32897), None),             # 258 lists: the last fold block takes 2
+    ("medium_fp8", dict(vocab=17000), "1"),             # tiled lm_head: 67 runs of one tile
+])
+def test_draft_many_candidate_lists(name, changes, tpb, monkeypatch):
+    """Many candidate lists per row: more than 64 go to the merge kernel's
+    256-thread block, more than 256 are first folded 64 at a time (16 best
+    keys of each run of lists).  Same checks as the default workloads."""
+    if tpb:
+        monkeypatch.setenv("DFLASH2_LMHEAD_TILES_PER_BLOCK", tpb)
+    w = synth.get(name).replace(**changes)
+    g = DraftRun(w)
+    try:
+        _, res = oracle_for(w, g.W)
+        check_step(g, res, range(w.batch))
+    finally:
+        g.close()
+
+
 @pytest.mark.parametrize("splits", ["1", "8"])
 def test_draft_tiled_192_row_tiles(splits, monkeypatch):
     """fp8 tiled GEMMs on 192-row block tiles (three accumulator row blocks

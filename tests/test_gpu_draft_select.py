@@ -4,10 +4,11 @@ dflash2_select_path on the same inputs: bit-identical candidate ids and
 values, paths, draft tokens and path scores.  The two-call path is checked
 against the oracle in test_gpu_draft.py, so this pins the fused one to the
 oracle too.  Covered: candidate lists of the weight-streaming lm_head
-(k <= 16 per 128-id group; more than 64 lists per row keep the separate
-merge kernel) and of the tiled one (16 per vocabulary run), 1..15 positions per sequence, a transformed
-logit (multiplier and soft cap), and k > 16, where the merge keeps its own
-kernel."""
+(k <= 16 per 128-id group; 65-256 lists per row keep the separate merge
+kernel, more than 256 are first folded 64 at a time) and of the
+tiled one (16 per vocabulary run), 1..15 positions per sequence, a
+transformed logit (multiplier and soft cap), and k > 16, where the merge
+keeps its own kernel."""
 import numpy as np
 import pytest
 import torch
@@ -26,6 +27,7 @@ CASES = [
     ("small_bf16", dict(block_size=2)),
     ("small_bf16", dict(vocab=8192)),    # 64 lists per row: the most the fused merge takes
     ("small_bf16", dict(vocab=8193)),    # 65 lists: the separate merge kernel
+    ("small_bf16", dict(vocab=40000, top_k=8)),   # 313 lists of 8 keys: folded to 5 first
     ("medium_fp8", {}),
     ("medium_bf16", dict(block_size=16)),
     ("dense27b_bf16", {}),
