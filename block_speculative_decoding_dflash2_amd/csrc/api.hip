@@ -266,7 +266,7 @@ Plan make_plan(const dflash2_config& c, int B, int64_t Mn) {
   // candidate lists: the weight-streaming lm_head writes groups x k keys per
   // row, the tiled one at most groups lists of 16
   p.off_cand = take(size_t(p.Mh) * p.groups * std::max(c.selector_top_k, 16) * 8);
-  // their first fold (k <= 16, more than 64 lists per row): 16 keys per 64 lists
+  // their first fold (k <= 16, more than 256 lists per row): 16 keys per 64 lists
   p.off_cand2 = take(size_t(p.Mh) * topk_premerge_lists(p.groups) * 16 * 8);
   // dynamic convolution: each conv site's input rows, float32
   p.off_hpre = gk > 0 ? take(size_t(p.M) * H * 4) : 0;
