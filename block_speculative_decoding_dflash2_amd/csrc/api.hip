@@ -78,6 +78,8 @@ bool rows_ok(int32_t batch, int32_t block_size) {
 }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+// The kernels read weights, activations and caches 16 bytes at a time.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int act_bytes(const dflash2_config& c) { return c.weight_dtype == DFLASH2_FP32 ? 4 : 2; }
@@ -382,6 +384,10 @@ dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weight
   const bool fp8 = c.weight_dtype == DFLASH2_FP8_E4M3;
   if (fp8 && (!w.lm_head_scale || !w.proj_scale))
     return fail(DFLASH2_ERR_INVALID_ARG, "create: fp8 weights need scales");
+  for (const void* q : {w.embed, w.lm_head, static_cast<const void*>(w.lm_head_scale), w.proj,
+                        static_cast<const void*>(w.proj_scale), w.proj_norm, w.final_norm,
+                        static_cast<const void*>(w.sel_tl), static_cast<const void*>(w.sel_tr)})
+    if (!aligned16(q)) return fail(DFLASH2_ERR_INVALID_ARG, "create: weight pointers must be 16-byte aligned");
   for (int l = 0; l < c.num_layers; ++l) {
     const dflash2_layer_weights& L = w.layers[l];
     const bool dyn = c.conv_group_size > 0;
@@ -391,6 +397,14 @@ dflash2_status dflash2_create(const dflash2_config* config, const dflash2_weight
     if (fp8 && (!L.wqkv_scale || !L.wo_scale || !L.w_gate_up_scale || !L.w_down_scale ||
                 (dyn && (!L.dconv_attn_scale || !L.dconv_ffn_scale))))
       return fail(DFLASH2_ERR_INVALID_ARG, "create: fp8 weights need scales (layer %d)", l);
+    for (const void* q : {L.attn_norm, L.wqkv, static_cast<const void*>(L.wqkv_scale), L.wo,
+                          static_cast<const void*>(L.wo_scale), L.ffn_norm, L.w_gate_up,
+                          static_cast<const void*>(L.w_gate_up_scale), L.w_down,
+                          static_cast<const void*>(L.w_down_scale), L.conv_attn, L.conv_ffn, L.dconv_attn,
+                          static_cast<const void*>(L.dconv_attn_scale), L.dconv_ffn,
+                          static_cast<const void*>(L.dconv_ffn_scale)})
+      if (!aligned16(q))
+        return fail(DFLASH2_ERR_INVALID_ARG, "create: weight pointers must be 16-byte aligned (layer %d)", l);
   }
   dflash2_handle* h = new dflash2_handle;
   h->cfg = c;
@@ -433,6 +447,10 @@ static dflash2_status draft_impl(dflash2_handle* handle, hipStream_t stream, int
   if (!anchor_ids || !new_offsets || !ctx_lens || !k_cache || !v_cache || !topk_ids || !topk_vals ||
       (max_new_rows > 0 && !new_taps))
     return fail(DFLASH2_ERR_INVALID_ARG, "draft_block: null pointer argument");
+  if (!aligned16(new_taps) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(debug_logits) ||
+      !aligned16(debug_hidden))
+    return fail(DFLASH2_ERR_INVALID_ARG,
+                "draft_block: new_taps, the caches and the debug outputs must be 16-byte aligned");
   const Plan P = make_plan(c, batch, max_new_rows);
   if (!workspace || workspace_bytes < P.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
     return fail(DFLASH2_ERR_WORKSPACE, "draft_block: workspace needs %zu bytes, 256-aligned", P.total);

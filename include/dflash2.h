@@ -166,7 +166,8 @@ typedef struct dflash2_handle dflash2_handle;
  * divide hidden, selector_top_k outside 1..min(64, vocab), selector_rank
  * outside 1..256, mask_token_id outside [0, vocab), an unknown weight_dtype,
  * a null weight (the static conv taps when conv_group_size is 0, the dynamic
- * ones otherwise), a missing fp8 scale, a non-finite rms_eps, rope_theta,
+ * ones otherwise), a missing fp8 scale, a weight or scale pointer that is not
+ * 16-byte aligned (the kernels read 16 bytes at a time), a non-finite rms_eps, rope_theta,
  * input_embedding_scale or softcap, an output_multiplier that is not finite
  * and > 0 (top-k ranks the raw logits and transforms the kept values, which
  * needs a strictly increasing transform), and (UNSUPPORTED) any contraction
@@ -215,7 +216,9 @@ dflash2_status dflash2_workspace_size(const dflash2_handle* handle, int32_t batc
  *   debug_hidden [device, nullable] float [batch, block_size, hidden]: the
  *               residual stream after the last layer.
  *   workspace   [device] >= dflash2_workspace_size bytes, 256-byte aligned;
- *               scratch only, contents need no initialisation. */
+ *               scratch only, contents need no initialisation.
+ * new_taps, k_cache, v_cache, debug_logits and debug_hidden must be 16-byte
+ * aligned (DFLASH2_ERR_INVALID_ARG otherwise). */
 dflash2_status dflash2_draft_block(dflash2_handle* handle, hipStream_t stream, int32_t batch,
                                    const int32_t* anchor_ids, const void* new_taps,
                                    const int32_t* new_offsets, const int32_t* ctx_lens,

@@ -131,6 +131,32 @@ def _handle(cfg):
     return h, (w, keep)
 
 
+def test_create_rejects_misaligned_weights():
+    """Weight and scale pointers must be 16-byte aligned."""
+    cfg = dict(BASE)
+    for field in ("lm_head", "embed", "proj_norm"):
+        w, lw = _fake_weights(cfg["num_layers"])
+        setattr(w, field, 0x1008)
+        h = ctypes.c_void_p()
+        assert L.lib.dflash2_create(ctypes.byref(config_struct(cfg)), ctypes.byref(w), ctypes.byref(h)) \
+            == L.DFLASH2_ERR_INVALID_ARG, field
+        assert "16-byte aligned" in L.dflash2_last_error()
+    w, lw = _fake_weights(cfg["num_layers"])
+    lw[0].w_down = 0x1004
+    h = ctypes.c_void_p()
+    assert L.lib.dflash2_create(ctypes.byref(config_struct(cfg)), ctypes.byref(w), ctypes.byref(h)) \
+        == L.DFLASH2_ERR_INVALID_ARG
+    assert "16-byte aligned" in L.dflash2_last_error()
+    cfg8 = dict(BASE, weight_dtype="fp8")
+    w8, lw8 = _fake_weights(cfg8["num_layers"], fp8=True)
+    assert L.lib.dflash2_create(ctypes.byref(config_struct(cfg8)), ctypes.byref(w8), ctypes.byref(h)) == 0
+    L.lib.dflash2_destroy(h)
+    w8.lm_head_scale = 0x1004
+    assert L.lib.dflash2_create(ctypes.byref(config_struct(cfg8)), ctypes.byref(w8), ctypes.byref(h)) \
+        == L.DFLASH2_ERR_INVALID_ARG
+    assert "16-byte aligned" in L.dflash2_last_error()
+
+
 def test_workspace_size_and_draft_argument_errors():
     h, keep = _handle(BASE)
     try:
@@ -155,6 +181,15 @@ def test_workspace_size_and_draft_argument_errors():
         with pytest.raises(L.DFlash2Error) as e:
             L.dflash2_draft_block(h, None, 0, p, p, p, p, 32, p, p, p, p, None, None, p, n1)
         assert e.value.status == L.DFLASH2_ERR_SHAPE
+        # misaligned taps, cache or debug output
+        for args in ((p, p + 2, p, p, 32, p, p), (p, p, p, p, 32, p + 8, p), (p, p, p, p, 32, p, p + 4)):
+            with pytest.raises(L.DFlash2Error) as e:
+                L.dflash2_draft_block(h, None, 1, *args, p, p, None, None, p, n1)
+            assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
+            assert "16-byte aligned" in L.dflash2_last_error()
+        with pytest.raises(L.DFlash2Error) as e:
+            L.dflash2_draft_block(h, None, 1, p, p, p, p, 32, p, p, p, p, p + 4, None, p, n1)
+        assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
         with pytest.raises(L.DFlash2Error) as e:
             L.dflash2_select_path(h, None, 1, p, None, p, p, p, None, None)
         assert e.value.status == L.DFLASH2_ERR_INVALID_ARG
