@@ -182,7 +182,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
             for (int u = 0; u < 2; ++u) {
               const float gt = acc[i][j][4 * q + e + u];
               const float up = acc[i + 2][j][4 * q + e + u];
-              y[u] = gt / (1.0f + expf(-gt)) * up;
+              // hardware exponential (a few float ulp; the outputs are bf16):
+              // 621 -> 605 us for the fp8 high-batch gate/up projection
+              y[u] = gt / (1.0f + __expf(-gt)) * up;
             }
             o[e / 2] = uint32_t(f32_to_bf16(y[0])) | (uint32_t(f32_to_bf16(y[1])) << 16);
           }
