@@ -33,7 +33,7 @@ template <> struct AttnFrag<bf16_t> {
   __device__ static void from_f32(frag& f, const float (&p)[8]) {
     u32x4 u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) u[j] = uint32_t(f32_to_bf16(p[2 * j])) | (uint32_t(f32_to_bf16(p[2 * j + 1])) << 16);
+    for (int j = 0; j < 4; ++j) u[j] = f32x2_to_bf16x2(p[2 * j], p[2 * j + 1]);
     f.v = __builtin_bit_cast(bf16x8, u);
   }
 };

@@ -21,12 +21,16 @@ constexpr int WAVE = 64;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round to nearest even (inputs are finite).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
+// Two floats to two bf16 (low half: lo), rounded to nearest even by the
+// hardware conversion (one instruction per pair; the same bits as adding
+// 0x7FFF plus the kept lsb and truncating, for the finite inputs here).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+  typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_hw{lo, hi}, bf16x2_hw));
 }
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return bf16_t(f32x2_to_bf16x2(f, 0.f) & 0xFFFFu); }
 
 template <typename T> struct Act;
 template <> struct Act<float> {

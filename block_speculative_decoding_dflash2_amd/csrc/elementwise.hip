@@ -49,8 +49,8 @@ template <> struct Act4<bf16_t> {
   }
   __device__ static void store(bf16_t* p, int64_t i, f32x4 v) {
     uint2 u;
-    u.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
-    u.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+    u.x = f32x2_to_bf16x2(v[0], v[1]);
+    u.y = f32x2_to_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(p + i) = u;
   }
 };

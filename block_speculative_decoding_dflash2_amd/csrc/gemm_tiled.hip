@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
               // 621 -> 605 us for the fp8 high-batch gate/up projection
               y[u] = gt / (1.0f + __expf(-gt)) * up;
             }
-            o[e / 2] = uint32_t(f32_to_bf16(y[0])) | (uint32_t(f32_to_bf16(y[1])) << 16);
+            o[e / 2] = f32x2_to_bf16x2(y[0], y[1]);
           }
           bf16_t* dst = out + int64_t(m) * F + f;
           if (f + 3 < F && (F & 3) == 0) {
@@ -241,10 +241,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
             y1[u] = xb;
           }
         }
-        const u32x2 lo = {uint32_t(f32_to_bf16(y0[0])) | (uint32_t(f32_to_bf16(y0[1])) << 16),
-                          uint32_t(f32_to_bf16(y0[2])) | (uint32_t(f32_to_bf16(y0[3])) << 16)};
-        const u32x2 hi = {uint32_t(f32_to_bf16(y1[0])) | (uint32_t(f32_to_bf16(y1[1])) << 16),
-                          uint32_t(f32_to_bf16(y1[2])) | (uint32_t(f32_to_bf16(y1[3])) << 16)};
+        const u32x2 lo = {f32x2_to_bf16x2(y0[0], y0[1]),
+                          f32x2_to_bf16x2(y0[2], y0[3])};
+        const u32x2 hi = {f32x2_to_bf16x2(y1[0], y1[1]),
+                          f32x2_to_bf16x2(y1[2], y1[3])};
         if (head < e.nq) {
           bf16_t* dst = qo + (int64_t(m) * e.nq + head) * d;
           *reinterpret_cast<u32x2*>(dst + ci) = lo;
