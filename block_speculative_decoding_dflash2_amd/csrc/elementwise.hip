@@ -120,11 +120,21 @@ __global__ __launch_bounds__(256) void resconv_kernel(NormArgs p) {
   typedef typename X::V V;
   __shared__ float red[16];
   const int rows = p.rows_dev ? min(*p.rows_dev, p.rows) : p.rows;
-  const int r = blockIdx.x;
+  int r = blockIdx.x, cb = blockIdx.y;
+  if (p.remap_cb > 0) {
+    // blocks go to the 8 XCDs round-robin; XCD x runs tiles [x per, (x + 1) per)
+    // with the column block fastest, so the neighbour rows the convolution
+    // reads were just loaded into the same L2
+    const int per = int(gridDim.x >> 3);
+    const int g = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
+    r = g / p.remap_cb;
+    cb = g - r * p.remap_cb;
+    if (r >= p.rows) return;
+  }
   if (r >= rows) return;
   const int t = r % p.bs, b = r / p.bs;
   const int H = p.H;
-  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * VEC;
+  const int c = (cb * blockDim.x + threadIdx.x) * VEC;
   const T* E = static_cast<const T*>(p.embed);
   const T* C = static_cast<const T*>(p.conv);
 
@@ -172,10 +182,10 @@ __global__ __launch_bounds__(256) void resconv_kernel(NormArgs p) {
   const int nslots = norm_col_blocks_dev(H);
   if (VEC == 1) {
     const float ss = block_sum(X::sq(y), red);
-    if (threadIdx.x == 0) p.sumsq[int64_t(orow) * nslots + blockIdx.y] = ss;
+    if (threadIdx.x == 0) p.sumsq[int64_t(orow) * nslots + cb] = ss;
   } else {
     const float ss = wave_sum(X::sq(y));
-    const int slot = blockIdx.y * (256 * VEC / 256) + int(threadIdx.x) / WAVE;
+    const int slot = cb * (256 * VEC / 256) + int(threadIdx.x) / WAVE;
     if ((threadIdx.x & (WAVE - 1)) == 0 && slot < nslots) p.sumsq[int64_t(orow) * nslots + slot] = ss;
   }
 }
@@ -370,11 +380,16 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluArgs p) {
 
 int norm_col_blocks(int H) { return norm_col_blocks_dev(H); }
 
-void launch_norm(bool f32, const NormArgs& a, hipStream_t s) {
+void launch_norm(bool f32, const NormArgs& a0, hipStream_t s) {
   // few rows: one element per thread (more blocks, shorter chains); many
-  // rows: four per thread (16-byte accesses)
+  // rows: four per thread (16-byte accesses), tiles dealt to the XCDs in
+  // contiguous runs
+  NormArgs a = a0;
   const bool wide = a.rows > 64;
-  const dim3 grid(a.rows, wide ? (a.H + 1023) / 1024 : norm_col_blocks(a.H));
+  const int cbs = wide ? (a.H + 1023) / 1024 : norm_col_blocks(a.H);
+  const int64_t tiles = int64_t(a.rows) * cbs;
+  a.remap_cb = (wide && tiles < (int64_t(1) << 30)) ? cbs : 0;
+  const dim3 grid = a.remap_cb ? dim3(unsigned((tiles + 7) / 8 * 8)) : dim3(a.rows, cbs);
   if (f32) {
     if (wide) hipLaunchKernelGGL((resconv_kernel<float, 4>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((resconv_kernel<float, 1>), grid, dim3(256), 0, s, a);

@@ -95,6 +95,9 @@ struct NormArgs {
   void* n_out;                    // act [out rows][H]: gain * y; row map below
   float* sumsq;                   // [out rows][col_blocks] sums of y^2
   int t_first;                    // slots t < t_first produce no n_out / sumsq row
+  // > 0: 1D grid of rows x remap_cb column blocks dealt to the XCDs in
+  // contiguous runs (a row and its neighbour rows share an XCD's L2); 0: grid (rows, column blocks)
+  int remap_cb;
 };
 
 struct QkvEpiArgs {
