@@ -369,12 +369,14 @@ __global__ __launch_bounds__(256) void verify_partial_kernel(VerifyArgs p) {
     const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
     const int nt = blockDim.x;
     int i = a0 + threadIdx.x;
-    for (; i + 3 * nt < a1; i += 4 * nt) {  // four loads in flight per thread
-      f32x4 x[4];
+    // eight non-temporal 16-byte loads in flight per thread (four: fp8
+    // high-batch scan 210 against 203 us, batched 46 against 43 us)
+    for (; i + 7 * nt < a1; i += 8 * nt) {
+      f32x4 x[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = z4[i + u * nt];
+      for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(z4 + i + u * nt);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint64_t kk = rank_key(x[u][e], uint32_t(4 * (i + u * nt) + e));
