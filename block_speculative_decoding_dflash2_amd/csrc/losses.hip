@@ -72,18 +72,19 @@ __global__ __launch_bounds__(256) void loss_rows_kernel(LossArgs p) {
     }
   };
   if ((p.V & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0) {
-    // chunks are multiples of 256 ids: 16-byte loads, four in flight
+    // chunks are multiples of 256 ids: non-temporal 16-byte loads, eight in
+    // flight (a thread visits its values in the same order as with four)
     const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
     const int a0 = v0 >> 2, a1 = v1 >> 2;
-    for (int i0 = a0 + threadIdx.x; i0 < a1; i0 += 4 * blockDim.x) {
-      f32x4 x[4];
+    for (int i0 = a0 + threadIdx.x; i0 < a1; i0 += 8 * blockDim.x) {
+      f32x4 x[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * blockDim.x;
-        x[u] = i < a1 ? z4[i] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        x[u] = i < a1 ? __builtin_nontemporal_load(z4 + i) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
         if (i0 + u * int(blockDim.x) < a1) {
           add(x[u][0]); add(x[u][1]); add(x[u][2]); add(x[u][3]);
         }
