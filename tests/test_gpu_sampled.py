@@ -136,6 +136,7 @@ def test_sampled_matches_oracle(B, bs, V, T, top_k, top_p):
     (5000, 0.3, 1.0, 1.0, 1000, 0.9),    # the k-th value tied > 2048 ways
     (5000, 0.3, 1.0, 1.0, 0, 0.97),      # full-vocabulary top-p over large ties
     (8192, 0.0, 1.0, 1.0, 7, 0.5),       # every logit equal (planted drafts aside)
+    (5000, 0.3, 1.0, 1.0, 20, 0.9),      # the 20th value tied many ways, top-p on top
 ])
 def test_sampled_ties(V, spread, quantum, T, top_k, top_p):
     log(f"sampled ties V={V} spread={spread} q={quantum} T={T} top_k={top_k} top_p={top_p}")
@@ -214,6 +215,7 @@ def test_sampled_is_lossless_on_gpu():
 
 @pytest.mark.parametrize("B,T,top_k,top_p,nseq", [
     (256, 1.0, 20, 0.95, 6),       # the batched fp8 shape, headline sampling settings
+    (1, 1.0, 20, 0.95, 1),         # the 27B-class shape, headline sampling settings
     (1, 1.0, 0, 0.95, 1),          # the 27B-class shape, top-p over the whole vocabulary
     (4, 0.8, 0, 1.0, 2),
 ])
@@ -224,6 +226,25 @@ def test_sampled_full_vocab(B, T, top_k, top_p, nseq):
     uni = synth.make_uniforms((B, bs), tag=15)
     seqs = np.linspace(0, B - 1, nseq).astype(int)
     _check(drafts, z, uni, T, top_k, top_p, seqs=seqs, max_ambiguous=0.0)
+
+
+@pytest.mark.parametrize("top_k", [1, 20, 31])
+def test_sampled_sorted_rows(top_k):
+    """Rows whose largest values sit at the end of the row (ascending
+    logits) or at its start (descending), so the first ids the top-k pass
+    samples say nothing about the rest; plus a row with NaN, +inf and -inf
+    entries."""
+    B, bs, V = 4, 4, 30000
+    log(f"sampled sorted rows V={V} top_k={top_k}")
+    drafts, z = synth.make_sampling_inputs(B, bs, V, tag=21)
+    ramp = np.linspace(-8.0, 8.0, V, dtype=np.float32)
+    z[0] = ramp
+    z[1] = ramp[::-1]
+    z[2, :, ::7] = np.nan
+    z[2, :, 5] = np.inf
+    z[2, :, 11::13] = -np.inf
+    uni = synth.make_uniforms((B, bs), tag=22)
+    _check(drafts, z, uni, 1.0, top_k, 0.95)
 
 
 def test_sampled_deterministic():
