@@ -144,21 +144,23 @@ __device__ void sv_find(SvShared& sh, int nb, bool by_mass, double X, uint64_t b
   __syncthreads();
 }
 
-// Calls f(id, value) for every element of the row, four loads in flight.
+// Calls f(id, value) for every element of the row, eight 16-byte loads in
+// flight per thread (a row is read by one block, so the loads in flight set
+// its rate).
 template <class F>
 __device__ __forceinline__ void sv_for_row(const float* __restrict__ z, int V, bool vec, F&& f) {
   if (vec) {
     const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
     const int n4 = V >> 2;
-    for (int i0 = threadIdx.x; i0 < n4; i0 += 4 * SV_THREADS) {
-      f32x4 x[4];
+    for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * SV_THREADS) {
+      f32x4 x[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * SV_THREADS;
-        x[u] = i < n4 ? z4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        x[u] = i < n4 ? __builtin_nontemporal_load(z4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * SV_THREADS;
         if (i < n4) {
 #pragma unroll
