@@ -159,6 +159,11 @@ Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
     // weight row: the 5120 x 25600 feature projection measured 55 us with 480
     // blocks of 4288 bytes per row and 43 us with 1000 blocks of 2048 bytes
     // (both by this cost model's count the first was cheaper).
+    int64_t max_row_bytes = kStreamMaxRowBytes;
+    if (const char* env = std::getenv("DFLASH2_STREAM_MAX_ROW_BYTES")) {
+      const int v = std::atoi(env);
+      if (v >= 256 && v <= (1 << 20)) max_row_bytes = v;
+    }
     const int wb = dtype == 0 ? 4 : (dtype == 1 ? 2 : 1);
     const int max_s = std::max(1, std::min(64, K / 256));
     double best_cost = 1e300;
@@ -166,7 +171,7 @@ Split plan_split(int dtype, int M, int N, int K, int groups = 1) {
     for (int c = 1; c <= max_s; ++c) {
       const int64_t ks = cdiv(cdiv(K, c), 32) * 32;
       if (cdiv(K, ks) != c) continue;
-      const bool capped = ks * wb <= kStreamMaxRowBytes;
+      const bool capped = ks * wb <= max_row_bytes;
       const double cost = double(cdiv(blocks * c, target)) * double(ks + overhead);
       if ((capped && !best_capped) || (capped == best_capped && cost < best_cost * 0.999)) {
         best_cost = cost;

@@ -38,14 +38,17 @@
  *     (1..64), read at each dflash2_draft_block call, sets how many
  *     256-id vocabulary tiles one lm_head block sweeps when the batch has
  *     more than 64 rows (default: chosen from the shapes), and
- *     DFLASH2_TILED_MAX_SPLITS (1..16, default 8), read by
+ *     DFLASH2_TILED_MAX_SPLITS (1..16, default 16), read by
  *     dflash2_workspace_size and dflash2_draft_block, caps the K splits of
  *     those batches' linears (one
  *     split lets the GEMM apply SwiGLU and the QKV RoPE itself), and
  *     DFLASH2_STREAM_BLOCK_OVERHEAD (0..65536, default 256), read by the same
  *     calls, is the fixed cost of one weight-streaming block (batches of at
- *     most 64 rows), in k, in the model that picks their K splits.  Results
- *     agree to rounding either way.
+ *     most 64 rows), in k, in the model that picks their K splits, and
+ *     DFLASH2_STREAM_MAX_ROW_BYTES (256..1048576, default 3072), read by the
+ *     same calls, is the longest stretch of one weight row a streaming block
+ *     reads (the planner prefers splits that keep within it).  Results agree
+ *     to rounding either way.
  *   - Every call returns DFLASH2_OK or an error code; on error nothing was
  *     enqueued and dflash2_last_error() (thread-local) describes it.  Device
  *     data (ids, lengths, offsets) cannot be checked on the host; kernels
